@@ -1,0 +1,232 @@
+"""MI355X-native KDA (Kimi Delta Attention) token mixer.
+
+A thin Python binding over the C ABI of ``libkda.so`` (``include/kda.h``).
+Every step of the mixer runs in the library's HIP kernels; this module only
+checks tensor dtypes/shapes, passes device pointers and the current HIP
+stream, and allocates the update-card workspace with PyTorch.  There is no
+CPU or PyTorch fallback: if the library is missing, every call raises.
+
+Entry points (same names as the C ABI, minus the ``kda_`` prefix):
+    workspace_size, chunk_prepare, chunk_scan, segment_summarize,
+    segment_combine, decode_step
+Conveniences built from them: prefill, segmented_prefill.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "workspace too small",
+          4: "HIP runtime error"}
+EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_segment_summarize",
+           "kda_segment_combine", "kda_decode_step", "kda_status_string")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({code})")
+        self.code = code
+
+
+class KdaProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("heads", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("log_alpha_min", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_91_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        PP = ctypes.POINTER(KdaProblem)
+        L.kda_workspace_size.argtypes = [PP]
+        L.kda_workspace_size.restype = SZ
+        L.kda_chunk_prepare.argtypes = [PP, P, P, P, P, P, P, SZ, P]
+        L.kda_chunk_scan.argtypes = [PP, P, SZ, P, P, P, P, P]
+        L.kda_segment_summarize.argtypes = [PP, P, SZ, P, P, P]
+        L.kda_segment_combine.argtypes = [I64, I32, I32, I32, I32, P, P, P, P, P, P]
+        L.kda_decode_step.argtypes = [I64, I32, I32, I32, I32, F32, P, P, P, P, P, P, P, P, P]
+        for f in EXPORTS[1:-1]:
+            getattr(L, f).restype = I32
+        L.kda_status_string.argtypes = [I32]
+        L.kda_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise KdaError(fn, code)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return KDA_BF16
+    if dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v/g must be bfloat16 or float32, got {dtype}")
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if not x.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not x.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def problem(batch: int, seqlen: int, heads: int, dk: int, dv: int, io_dtype: int, log_alpha_min: float,
+            chunk: int = 64) -> KdaProblem:
+    return KdaProblem(batch, seqlen, heads, dk, dv, chunk, io_dtype, float(log_alpha_min))
+
+
+def _problem_of(q, v, log_alpha_min, chunk=64) -> KdaProblem:
+    B, T, H, dk = q.shape
+    return problem(B, T, H, dk, v.shape[-1], _io_code(q.dtype), log_alpha_min, chunk)
+
+
+def workspace_size(p: KdaProblem) -> int:
+    n = lib().kda_workspace_size(ctypes.byref(p))
+    if n == 0 and p.batch * p.heads * p.seqlen > 0:
+        raise KdaError("kda_workspace_size", 2)
+    return n
+
+
+def chunk_prepare(q, k, v, log_alpha, beta, log_alpha_min: float, workspace=None, stream=None):
+    """Stage 1: update cards for every chunk.  Returns the workspace (uint8 tensor)."""
+    torch = _torch()
+    p = _problem_of(q, v, log_alpha_min)
+    nbytes = workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check("kda_chunk_prepare", lib().kda_chunk_prepare(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def chunk_scan(workspace, g, log_alpha_min: float, state_in=None, out=None, state_out=None,
+               want_state: bool = True, stream=None):
+    """Stage 2: ordered hand-off + gated read-out.  Returns (out, state_out)."""
+    torch = _torch()
+    B, T, H, dv = g.shape
+    p = problem(B, T, H, dv, dv, _io_code(g.dtype), log_alpha_min)
+    if out is None:
+        out = torch.empty_like(g)
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, dv, dv), dtype=torch.float32, device=g.device)
+    _check("kda_chunk_scan", lib().kda_chunk_scan(
+        ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(g), _ptr(state_in), _ptr(out),
+        _ptr(state_out), _stream(stream)))
+    return out, state_out
+
+
+def segment_summarize(workspace, batch: int, seqlen: int, heads: int, dk: int, io_dtype, log_alpha_min: float,
+                      stream=None):
+    """(transition [B,H,dk,dk], zero_state [B,H,dk,dv]) of each (row, head) from its cards."""
+    torch = _torch()
+    p = problem(batch, seqlen, heads, dk, dk, _io_code(io_dtype), log_alpha_min)
+    A = torch.empty((batch, heads, dk, dk), dtype=torch.float32, device=workspace.device)
+    Bz = torch.empty((batch, heads, dk, dk), dtype=torch.float32, device=workspace.device)
+    _check("kda_segment_summarize", lib().kda_segment_summarize(
+        ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(A), _ptr(Bz), _stream(stream)))
+    return A, Bz
+
+
+def segment_combine(transition, zero_state, state_init=None, stream=None):
+    """In-order merge.  transition [B,n,H,dk,dk], zero_state [B,n,H,dk,dv] ->
+    (state entering each segment [B,n,H,dk,dv], final state [B,H,dk,dv])."""
+    torch = _torch()
+    B, n, H, dk, _ = transition.shape
+    dv = zero_state.shape[-1]
+    seg_in = torch.empty_like(zero_state)
+    fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=zero_state.device)
+    _check("kda_segment_combine", lib().kda_segment_combine(
+        B, n, H, dk, dv, _ptr(transition), _ptr(zero_state), _ptr(state_init), _ptr(seg_in), _ptr(fin),
+        _stream(stream)))
+    return seg_in, fin
+
+
+def decode_step(q, k, v, log_alpha, beta, g, state, log_alpha_min: float, out=None, stream=None):
+    """One token per sequence: q,k,log_alpha [N,H,dk]; v,g [N,H,dv]; beta [N,H];
+    state [N,H,dk,dv] fp32 updated in place.  Returns out [N,H,dv]."""
+    torch = _torch()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty_like(g)
+    _check("kda_decode_step", lib().kda_decode_step(
+        N, H, dk, dv, _io_code(q.dtype), float(log_alpha_min), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+        _ptr(beta), _ptr(g), _ptr(state), _ptr(out), _stream(stream)))
+    return out
+
+
+def prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, workspace=None, stream=None):
+    """Chunked prefill: prepare + scan.  Returns (out, final state)."""
+    ws = chunk_prepare(q, k, v, log_alpha, beta, log_alpha_min, workspace=workspace, stream=stream)
+    return chunk_scan(ws, g, log_alpha_min, state_in=state_in, stream=stream)
+
+
+def segmented_prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, n_seg: int, state_in=None,
+                      workspace=None, stream=None):
+    """Context-parallel prefill on one GPU: the sequence [B, n_seg*Ts, H, d] is
+    treated as n_seg segments (extra batch rows), each summarised from its
+    cards, the summaries merged in order, and every segment's outputs computed
+    from its exact entering state.  Returns (out, final state)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if T % n_seg:
+        raise ValueError("sequence length must split into n_seg equal segments")
+    Ts = T // n_seg
+    seg = lambda x: x.view((B * n_seg, Ts) + tuple(x.shape[2:]))
+    ws = chunk_prepare(seg(q), seg(k), seg(v), seg(log_alpha), seg(beta), log_alpha_min, workspace=workspace,
+                       stream=stream)
+    A, Bz = segment_summarize(ws, B * n_seg, Ts, H, dk, q.dtype, log_alpha_min, stream=stream)
+    seg_in, fin = segment_combine(A.view(B, n_seg, H, dk, dk), Bz.view(B, n_seg, H, dk, dv), state_in,
+                                  stream=stream)
+    out, _ = chunk_scan(ws, seg(g), log_alpha_min, state_in=seg_in.view(B * n_seg, H, dk, dv),
+                        want_state=False, stream=stream)
+    return out.view(B, T, H, dv), fin
+
+
+def to_device(inp, device="cuda"):
+    """Upload a kda_inputs.KdaInputs workload (bf16 bit patterns reinterpreted, no rounding)."""
+    import numpy as np
+    torch = _torch()
+
+    def io(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a).to(device)
+
+    d = dict(q=io(inp.q), k=io(inp.k), v=io(inp.v), g=io(inp.g),
+             log_alpha=torch.from_numpy(inp.log_alpha).to(device), beta=torch.from_numpy(inp.beta).to(device))
+    d["state0"] = None if inp.state0 is None else torch.from_numpy(inp.state0).to(device)
+    return d

@@ -1,0 +1,171 @@
+// kda_api.hip -- the C ABI of libkda.so (declared in include/kda.h).
+//
+// Every entry point validates its arguments synchronously, before any
+// launch, maps them to the kernel argument blocks and launches on the
+// caller's stream.  Nothing here allocates or keeps state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.hpp"
+
+using namespace kda;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ptr must be non-null and 16-byte aligned when the array is non-empty
+bool ok_ptr(const void* p, bool nonempty) { return !nonempty || (p != nullptr && aligned16(p)); }
+// beta is only read one fp32 at a time: natural alignment suffices
+bool ok_beta(const void* p, bool nonempty) { return !nonempty || (p != nullptr && ((uintptr_t)p & 3u) == 0); }
+bool ok_opt_ptr(const void* p) { return p == nullptr || aligned16(p); }
+
+kda_status check_floor(float f, int chunk) {
+    // the floor keeps exp(chunk * |floor|) -- the largest decay factor folded
+    // into one chunk's operands -- below e^80, inside fp32/bf16 range
+    if (!(f < 0.0f) || !(f >= -80.0f / (float)chunk)) return KDA_ERR_INVALID_ARGUMENT;
+    return KDA_OK;
+}
+
+kda_status check_problem(const kda_problem* p) {
+    if (!p) return KDA_ERR_INVALID_ARGUMENT;
+    if (p->batch < 0 || p->seqlen < 0 || p->heads <= 0 || p->dk <= 0 || p->dv <= 0 || p->chunk <= 0)
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (p->io_dtype != KDA_F32 && p->io_dtype != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
+    if (p->chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (p->dk != p->dv || (p->dk != 64 && p->dk != 128)) return KDA_ERR_UNSUPPORTED;
+    const kda_status f = check_floor(p->log_alpha_min, p->chunk);
+    if (f != KDA_OK) return f;
+    const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
+    // grid sizes and offsets must fit the kernels' index arithmetic
+    if (p->batch * (int64_t)p->heads * (nc > 0 ? nc : 1) > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (nc > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+int64_t n_chunks(const kda_problem* p) { return (p->seqlen + p->chunk - 1) / p->chunk; }
+
+kda_status device_ready() {
+    int dev = 0;
+    return hipGetDevice(&dev) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t kda_workspace_size(const kda_problem* p) {
+    if (check_problem(p) != KDA_OK) return 0;
+    return (size_t)p->batch * (size_t)p->heads * (size_t)n_chunks(p) * card_bytes(p->io_dtype == KDA_BF16, p->dk);
+}
+
+kda_status kda_chunk_prepare(const kda_problem* p, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    const bool nonempty = p->batch > 0 && p->seqlen > 0;
+    if (!ok_ptr(q, nonempty) || !ok_ptr(k, nonempty) || !ok_ptr(v, nonempty) || !ok_ptr(log_alpha, nonempty) ||
+        !ok_beta(beta, nonempty) || !ok_ptr(workspace, nonempty))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (!nonempty) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    PrepareArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+    a.ws = static_cast<char*>(workspace);
+    a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p);
+    a.floor_ = p->log_alpha_min;
+    return hip_status(launch_prepare(p->io_dtype == KDA_BF16, p->dk, a, (hipStream_t)stream));
+}
+
+kda_status kda_chunk_scan(const kda_problem* p, const void* workspace, size_t workspace_bytes, const void* g,
+                          const float* state_in, void* out, float* state_out, void* stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->batch > 0 && p->seqlen > 0;
+    if (!ok_ptr(workspace, tokens) || !ok_ptr(g, tokens) || !ok_ptr(out, tokens) || !ok_opt_ptr(state_in) ||
+        !ok_opt_ptr(state_out))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (p->batch == 0 || (!tokens && !state_out)) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    ScanArgs a = {};
+    a.ws = static_cast<const char*>(workspace);
+    a.g = g; a.state_in = state_in; a.out = out; a.state_out = state_out;
+    a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p);
+    return hip_status(launch_scan(p->io_dtype == KDA_BF16, p->dk, false, a, (hipStream_t)stream));
+}
+
+kda_status kda_segment_summarize(const kda_problem* p, const void* workspace, size_t workspace_bytes,
+                                 float* transition, float* zero_state, void* stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    const bool rows = p->batch > 0;
+    if (!ok_ptr(workspace, rows && p->seqlen > 0) || !ok_ptr(transition, rows) || !ok_ptr(zero_state, rows))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (!rows) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    ScanArgs a = {};
+    a.ws = static_cast<const char*>(workspace);
+    a.transition = transition; a.zero_state = zero_state;
+    a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p);
+    return hip_status(launch_scan(p->io_dtype == KDA_BF16, p->dk, true, a, (hipStream_t)stream));
+}
+
+kda_status kda_segment_combine(int64_t B, int32_t n_seg, int32_t H, int32_t dk, int32_t dv, const float* transition,
+                               const float* zero_state, const float* state_init, float* seg_state_in,
+                               float* state_final, void* stream) {
+    if (B < 0 || n_seg < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (B * (int64_t)H * (dv / 16) > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    const bool segs = B > 0 && n_seg > 0;
+    if (!ok_ptr(transition, segs) || !ok_ptr(zero_state, segs) || !ok_ptr(seg_state_in, segs) ||
+        !ok_opt_ptr(state_init) || !ok_opt_ptr(state_final))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (B == 0 || (n_seg == 0 && !state_final)) return KDA_OK;
+    kda_status st = device_ready();
+    if (st != KDA_OK) return st;
+    CombineArgs a;
+    a.A = transition; a.Bz = zero_state; a.s0 = state_init; a.seg_in = seg_state_in; a.fin = state_final;
+    a.B = B; a.n_seg = n_seg; a.H = H; a.dk = dk; a.dv = dv;
+    return hip_status(launch_combine(a, (hipStream_t)stream));
+}
+
+kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype, float log_alpha_min,
+                           const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                           const void* g, float* state, void* out, void* stream) {
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (N * (int64_t)H > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    kda_status st = check_floor(log_alpha_min, 64);
+    if (st != KDA_OK) return st;
+    const bool any = N > 0;
+    if (!ok_ptr(q, any) || !ok_ptr(k, any) || !ok_ptr(v, any) || !ok_ptr(log_alpha, any) || !ok_beta(beta, any) ||
+        !ok_ptr(g, any) || !ok_ptr(state, any) || !ok_ptr(out, any))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!any) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.g = g; a.state = state; a.out = out;
+    a.N = N; a.H = H; a.floor_ = log_alpha_min;
+    return hip_status(launch_decode(io_dtype == KDA_BF16, dk, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

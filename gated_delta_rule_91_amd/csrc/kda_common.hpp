@@ -1,0 +1,122 @@
+// kda_common.hpp -- device-side building blocks shared by the KDA kernels
+// (gfx950 / CDNA4, wave64).
+//
+//  * bf16 <-> fp32 conversion (round to nearest even, NaN kept NaN)
+//  * the MFMA operand policy: bf16 operands use v_mfma_f32_16x16x32_bf16,
+//    fp32 operands use v_mfma_f32_16x16x4_f32; both accumulate in fp32
+//  * the layout of one "update card" (the per-chunk bundle the prepare
+//    kernel writes and the ordered hand-off kernel reads)
+//
+// MFMA 16x16 register layout (one wave, lane l, g = l / 16, n = l % 16):
+//   A operand : A[m = n][k = k0 + KF*g + e],  e < KF
+//   B operand : B[k = k0 + KF*g + e][n]
+//   C/D       : acc[v] = D[4*g + v][n],      v < 4
+// with KF = 8 (bf16, K step 32) or KF = 1 (fp32, K step 4).  A and B use the
+// same k assignment, so any consistent permutation of k is harmless.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 64;      // tokens per chunk
+constexpr int kThreads = 256;   // four waves per workgroup
+
+// ---- scalar conversions ---------------------------------------------------
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// ---- MFMA policy ------------------------------------------------------------
+template <typename E> struct MM;
+
+template <> struct MM<__bf16> {
+    static constexpr int KF = 8;      // k values per lane per step
+    static constexpr int KS = 32;     // k per MFMA
+    typedef bf16x8 frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static frag neg(frag a) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 u = __builtin_bit_cast(u32x4, a);
+        u ^= 0x80008000u;
+        return __builtin_bit_cast(frag, u);
+    }
+};
+
+template <> struct MM<float> {
+    static constexpr int KF = 1;
+    static constexpr int KS = 4;
+    typedef float frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static frag neg(frag a) { return -a; }
+};
+
+// Fragment at row `row`, k range [k0 + KF*g, k0 + KF*g + KF) of a row-major
+// matrix with leading dimension `ld` (elements).  Works for LDS and global
+// pointers; the address must be aligned to the fragment size.
+template <typename E>
+__device__ __forceinline__ typename MM<E>::frag ld_frag(const E* base, int ld, int row, int k0, int g) {
+    return *reinterpret_cast<const typename MM<E>::frag*>(base + (size_t)row * ld + k0 + MM<E>::KF * g);
+}
+
+// Four consecutive elements (8 B for bf16, 16 B for fp32) <-> fp32x4.
+__device__ __forceinline__ f32x4 ld4(const __bf16* p) {
+    bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(__bf16* p, f32x4 v) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// Two consecutive elements <-> fp32x2.
+__device__ __forceinline__ f32x2 ld2(const __bf16* p) {
+    bf16x2 x = *reinterpret_cast<const bf16x2*>(p);
+    return f32x2{(float)x[0], (float)x[1]};
+}
+__device__ __forceinline__ f32x2 ld2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
+__device__ __forceinline__ void st2(__bf16* p, float a, float b) {
+    *reinterpret_cast<bf16x2*>(p) = bf16x2{(__bf16)a, (__bf16)b};
+}
+__device__ __forceinline__ void st2(float* p, float a, float b) { *reinterpret_cast<f32x2*>(p) = f32x2{a, b}; }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// ---- update card --------------------------------------------------------------
+// One card per (batch row, head, chunk), for chunk length C = 64 and
+// d_k = d_v = DK.  E is the operand type of the ordered stage (bf16 or fp32).
+//   Wk  [C][DK]  row-major   Wk = T diag(beta) Kt         (A operand of U = Wv - Wk S)
+//   Qt  [C][DK]  row-major   q^ * e^gamma                  (A operand of O = Qt S + P U)
+//   KeT [DK][C]  row-major   (k^ * e^(gamma_C - gamma))^T  (A operand of S' = G S + Ke^T U)
+//   P   [C][C]   row-major   lower_incl(Qt Kh^T)           (A operand of P U)
+//   Wv  [DK/16][C/16][64][4] in accumulator order: the 16x16 tile (token tile
+//       mi, column tile ni) sits at ((ni*4 + mi)*64 + lane)*4, lane holding
+//       rows 4g..4g+3 of column n -- exactly the C operand of U's MFMA.
+//   GC  [DK] fp32            e^gamma_C, the chunk's total retention per key channel
+template <typename E, int DK>
+struct Card {
+    static constexpr int C = kChunk;
+    static constexpr size_t WK = 0;
+    static constexpr size_t QT = WK + (size_t)C * DK * sizeof(E);
+    static constexpr size_t KET = QT + (size_t)C * DK * sizeof(E);
+    static constexpr size_t P = KET + (size_t)DK * C * sizeof(E);
+    static constexpr size_t WV = P + (size_t)C * C * sizeof(E);
+    static constexpr size_t GC = WV + (size_t)C * DK * sizeof(E);
+    static constexpr size_t BYTES = ((GC + (size_t)DK * sizeof(float)) + 255) / 256 * 256;
+};
+
+}  // namespace kda

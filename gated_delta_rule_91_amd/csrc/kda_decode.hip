@@ -1,0 +1,123 @@
+// kda_decode.hip -- one decode step for N independent sequences: the
+// fixed-size memory is updated in place, no per-token cache grows
+// [devpress.csdn.net K3 article §十六: KDA keeps a recursive state rather
+// than per-token K/V; zuoshipin.com/article/18261 §二 for the step itself].
+//
+// Per (sequence, head), with S' = diag(e^lambda) S (retention with the floor):
+//   p = S'^T kh,  r = S'^T qh     (one sweep over S)
+//   u = beta (v - p)
+//   S <- S' + kh u^T              (in place)
+//   o = S^T qh = r + u (kh . qh); out = o * sigmoid(g)
+//
+// The step is bound by HBM: the fp32 state (64 KB per head at d = 128) is
+// read once and written once, and everything else is < 2 KB.  One workgroup
+// per (sequence, head); thread (column group cg, row group rg) keeps a
+// rows x 4-column block of S in registers between the read and the write.
+// The state streams with non-temporal loads/stores (it is larger than the
+// last-level cache), and the column partial sums of p and r are combined
+// across row groups through LDS.
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+namespace {
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
+    constexpr int DV = DK;
+    constexpr int CG = DV / 4;          // 4-column groups
+    constexpr int RG = kThreads / CG;   // row groups
+    constexpr int RPT = DK / RG;        // rows per thread
+    constexpr int EPL = DK / 64;        // elements per lane for the norm sweep
+
+    __shared__ float red[2][RG][DV];
+
+    const int t = threadIdx.x, lane = t & 63, cg = t % CG, rg = t / CG;
+    const size_t nh = blockIdx.x;
+    const E* q = reinterpret_cast<const E*>(a.q) + nh * DK;
+    const E* k = reinterpret_cast<const E*>(a.k) + nh * DK;
+    const E* v = reinterpret_cast<const E*>(a.v) + nh * DV;
+    const E* gp = reinterpret_cast<const E*>(a.g) + nh * DV;
+    const float* la = a.log_alpha + nh * DK;
+    float* S = a.state + nh * DK * DV;
+
+    // the state block first: RPT rows x 4 columns
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg * RPT + i) * DV + 4 * cg));
+
+    // norms and k.q, each wave on its own (no LDS)
+    float sk = 0.f, sq = 0.f, kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const float kk = to_f32(k[lane * EPL + e]), qq = to_f32(q[lane * EPL + e]);
+        sk += kk * kk; sq += qq * qq; kq += kk * qq;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        sk += __shfl_xor(sk, off);
+        sq += __shfl_xor(sq, off);
+        kq += __shfl_xor(kq, off);
+    }
+    const float rk = 1.0f / fmaxf(sqrtf(sk), 1e-6f), rq = 1.0f / fmaxf(sqrtf(sq), 1e-6f);
+    const float khqh = kq * rk * rq;
+    const float bt = a.beta[nh];
+
+    // retention and the two column sums over this thread's rows
+    float kh[RPT];
+    f32x4 pp = {0.f, 0.f, 0.f, 0.f}, rr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg * RPT + i;
+        const float dec = __expf(fmaxf(la[r], a.floor_));
+        kh[i] = to_f32(k[r]) * rk;
+        const float qh = to_f32(q[r]) * rq;
+        s[i] = s[i] * dec;
+        pp += s[i] * kh[i];
+        rr += s[i] * qh;
+    }
+    *reinterpret_cast<f32x4*>(&red[0][rg][4 * cg]) = pp;
+    *reinterpret_cast<f32x4*>(&red[1][rg][4 * cg]) = rr;
+    __syncthreads();
+    f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        p += *reinterpret_cast<const f32x4*>(&red[0][j][4 * cg]);
+        r += *reinterpret_cast<const f32x4*>(&red[1][j][4 * cg]);
+    }
+    const f32x4 vv = ld4(v + 4 * cg);
+    const f32x4 u = bt * (vv - p);
+
+    // corrective write, in place
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        __builtin_nontemporal_store(s[i] + kh[i] * u, reinterpret_cast<f32x4*>(S + (size_t)(rg * RPT + i) * DV + 4 * cg));
+
+    if (rg == 0) {
+        const f32x4 gg = ld4(gp + 4 * cg);
+        const f32x4 o = r + u * khqh;
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = o[e] * sigmoidf_(gg[e]);
+        st4(reinterpret_cast<E*>(a.out) + nh * DV + 4 * cg, y);
+    }
+}
+
+template <typename E, int DK>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+    const int64_t blocks = a.N * (int64_t)a.H;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_decode_kernel<E, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(bool bf16, int dk, const DecodeArgs& a, hipStream_t s) {
+    if (bf16) return dk == 128 ? launch_decode_t<__bf16, 128>(a, s) : launch_decode_t<__bf16, 64>(a, s);
+    return dk == 128 ? launch_decode_t<float, 128>(a, s) : launch_decode_t<float, 64>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,66 @@
+// kda_internal.hpp -- host-side launch entry points of the KDA kernels.
+// Each returns hipSuccess or the launch error; arguments were validated by
+// the C ABI layer (kda_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct PrepareArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    char* ws;
+    int64_t B, T;
+    int H, NC;
+    float floor_;
+};
+
+struct ScanArgs {
+    const char* ws;
+    const void* g;
+    const float* state_in;   // [B,H,dk,dv] or null
+    void* out;
+    float* state_out;        // [B,H,dk,dv] or null
+    float* transition;       // summary mode: [B,H,dk,dk]
+    float* zero_state;       // summary mode: [B,H,dk,dv]
+    int64_t B, T;
+    int H, NC;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const void* g;
+    float* state;
+    void* out;
+    int64_t N;
+    int H;
+    float floor_;
+};
+
+struct CombineArgs {
+    const float* A;
+    const float* Bz;
+    const float* s0;
+    float* seg_in;
+    float* fin;
+    int64_t B;
+    int n_seg, H, dk, dv;
+};
+
+size_t card_bytes(bool bf16, int dk);
+hipError_t launch_prepare(bool bf16, int dk, const PrepareArgs& a, hipStream_t s);
+hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s);
+hipError_t launch_decode(bool bf16, int dk, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace kda

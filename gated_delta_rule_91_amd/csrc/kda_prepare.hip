@@ -1,0 +1,394 @@
+// kda_prepare.hip -- stage 1 of the chunk method: one "update card" per
+// (batch row, head, chunk), all chunks in parallel.
+//
+// The pages name the card's contents -- forget gate, query/key
+// normalisation, decay, intra-chunk correction matrix -- and say they are
+// prepared ahead of the ordered stage [zuoshipin.com/article/18261 §四,
+// FlashKDA paragraph].  The algebra is derived from the recurrence:
+//
+//   lambda = max(log_alpha, floor); gamma = inclusive cumsum of lambda over
+//   the chunk, per key channel (the floor keeps e^{-gamma} <= e^{64|floor|},
+//   the bf16-range argument of zuoshipin §二)
+//   Qt = q^ e^gamma,  Kt = k^ e^gamma,  Kh = k^ e^-gamma,  Ke = k^ e^(gamma_C - gamma)
+//   L  = strict_lower(Kt Kh^T) (the intra-chunk correction matrix),
+//   P  = lower_incl(Qt Kh^T)
+//   T  = (I + diag(beta) L)^-1,  Wk = T diag(beta) Kt,  Wv = T diag(beta) V
+//
+// One workgroup (4 waves) per chunk-head.  Phases:
+//   A  coalesced loads (one wave-instruction = one token row), floored
+//      log-decay, per-channel cumulative sum (serial in registers, then a
+//      cross-group offset through LDS), q/k norms (wave reductions), decay
+//      folding; Kt/Kh/Qt to LDS, Ke^T and e^gamma_C straight to the card
+//   B  L and P on MFMA (10 lower tiles each)
+//   C  Qt and P to the card; diag(beta) L to LDS in fp32
+//   D  T by blocked substitution in fp32: 16x16 diagonal blocks by forward
+//      substitution, off-diagonal blocks with fp32 MFMA
+//   E  Wk and Wv on MFMA (block-lower-triangular T); Wv to the card in
+//      accumulator order, Wk through LDS to the card row-major
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+namespace {
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename E, int DK>
+struct PrepLds {
+    static constexpr int C = kChunk;
+    static constexpr int PAD = 16 / (int)sizeof(E);
+    static constexpr int LDR = DK + PAD;   // row-major [C][DK] tiles
+    static constexpr int LDT = C + PAD;    // transposed [DK][C] tiles and T
+    static constexpr int LDA = C + 4;      // fp32 [C][C] correction matrix / T
+    static constexpr size_t R0 = 0;
+    static constexpr size_t R_ROWMAJOR = (size_t)C * LDR * sizeof(E);
+    static constexpr size_t R_TRANS = (size_t)DK * LDT * sizeof(E);
+    static constexpr size_t RSZ = R_ROWMAJOR > R_TRANS ? R_ROWMAJOR : R_TRANS;
+    static constexpr size_t R1 = R0 + RSZ;
+    static constexpr size_t R2 = R1 + RSZ;
+    static constexpr size_t R2SZ = R_ROWMAJOR > (size_t)C * LDA * 4 ? R_ROWMAJOR : (size_t)C * LDA * 4;
+    static constexpr size_t R4 = R2 + R2SZ;
+    static constexpr size_t R4SZ = (size_t)C * LDT * sizeof(E);
+    static constexpr int NG = kThreads / (DK / 2);
+    static constexpr size_t TOT = R4 + R4SZ;                    // fp32 [NG][DK]
+    static constexpr size_t BETA = TOT + (size_t)NG * DK * 4;   // fp32 [C]
+    static constexpr size_t BYTES = BETA + (size_t)C * 4;
+};
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a) {
+    using M = MM<E>;
+    using CL = Card<E, DK>;
+    using LY = PrepLds<E, DK>;
+    constexpr int C = kChunk, KS = M::KS;
+    constexpr int CP = DK / 2;          // channel pairs: one lane per pair
+    constexpr int NG = kThreads / CP;   // token groups
+    constexpr int TPG = C / NG;         // tokens per group
+    constexpr int LDR = LY::LDR, LDT = LY::LDT, LDA = LY::LDA;
+    constexpr int NT = DK / 16;         // 16-wide column tiles
+
+    __shared__ __attribute__((aligned(16))) char lds[LY::BYTES];
+    E* sKt = reinterpret_cast<E*>(lds + LY::R0);     // phase A-B: Kt row-major
+    E* sKh = reinterpret_cast<E*>(lds + LY::R1);     // phase A-B: Kh row-major
+    E* sQt = reinterpret_cast<E*>(lds + LY::R2);     // phase A-C: Qt row-major
+    E* sKbT = reinterpret_cast<E*>(lds + LY::R0);    // phase C-E: (beta Kt)^T
+    E* sVbT = reinterpret_cast<E*>(lds + LY::R1);    // phase C-E: (beta V)^T
+    float* sA = reinterpret_cast<float*>(lds + LY::R2);   // phase C-D: diag(beta) L -> T (fp32)
+    E* sTb = reinterpret_cast<E*>(lds + LY::R4);     // phase D-E: T as MFMA operand
+    E* sWk = reinterpret_cast<E*>(lds + LY::R0);     // phase E: Wk staging
+    float* sTot = reinterpret_cast<float*>(lds + LY::TOT);
+    float* sBeta = reinterpret_cast<float*>(lds + LY::BETA);
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6, g = lane >> 4, n = lane & 15;
+
+    // block -> (b, chunk, h): heads fastest, so neighbouring workgroups read
+    // neighbouring 256-byte pieces of the same token rows
+    const int H = a.H, NC = a.NC;
+    const int64_t T = a.T;
+    const int64_t wg = blockIdx.x;
+    const int h = (int)(wg % H);
+    const int64_t rest = wg / H;
+    const int c = (int)(rest % NC);
+    const int64_t b = rest / NC;
+    const int64_t tok0 = (int64_t)c * C;
+    char* card = a.ws + (((size_t)b * H + h) * NC + c) * CL::BYTES;
+    const E* q = reinterpret_cast<const E*>(a.q);
+    const E* k = reinterpret_cast<const E*>(a.k);
+    const E* v = reinterpret_cast<const E*>(a.v);
+
+    // ---------------- phase A ----------------
+    const int cp = t % CP, grp = t / CP, c0 = 2 * cp;
+    float lam[TPG][2], qv[TPG][2], kv[TPG][2], vv[TPG][2];
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+        const int64_t tt = tok0 + grp * TPG + i;
+        if (tt < T) {
+            const size_t row = ((size_t)b * T + tt) * H + h;
+            const f32x2 l2 = *reinterpret_cast<const f32x2*>(a.log_alpha + row * DK + c0);
+            const f32x2 q2 = ld2(q + row * DK + c0), k2 = ld2(k + row * DK + c0), v2 = ld2(v + row * DK + c0);
+            lam[i][0] = fmaxf(l2[0], a.floor_);
+            lam[i][1] = fmaxf(l2[1], a.floor_);
+            qv[i][0] = q2[0]; qv[i][1] = q2[1];
+            kv[i][0] = k2[0]; kv[i][1] = k2[1];
+            vv[i][0] = v2[0]; vv[i][1] = v2[1];
+        } else {   // identity padding: lambda = 0, beta = 0, q = k = v = 0
+            lam[i][0] = lam[i][1] = 0.f;
+            qv[i][0] = qv[i][1] = kv[i][0] = kv[i][1] = vv[i][0] = vv[i][1] = 0.f;
+        }
+    }
+    if (t < C) {
+        const int64_t tt = tok0 + t;
+        sBeta[t] = (tt < T) ? a.beta[((size_t)b * T + tt) * H + h] : 0.f;
+    }
+    // inclusive cumulative log-decay inside the group
+    float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+        run0 += lam[i][0]; lam[i][0] = run0;
+        run1 += lam[i][1]; lam[i][1] = run1;
+    }
+    sTot[grp * DK + c0] = run0;
+    sTot[grp * DK + c0 + 1] = run1;
+    // q/k norms: reduce over the CP lanes that share this token group
+    float rq[TPG], rk[TPG];
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+        float sq = qv[i][0] * qv[i][0] + qv[i][1] * qv[i][1];
+        float sk = kv[i][0] * kv[i][0] + kv[i][1] * kv[i][1];
+#pragma unroll
+        for (int off = 1; off < CP; off <<= 1) {
+            sq += __shfl_xor(sq, off);
+            sk += __shfl_xor(sk, off);
+        }
+        rq[i] = 1.0f / fmaxf(sqrtf(sq), 1e-6f);
+        rk[i] = 1.0f / fmaxf(sqrtf(sk), 1e-6f);
+    }
+    __syncthreads();
+
+    float off0 = 0.f, off1 = 0.f, tot0 = 0.f, tot1 = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+        const float x0 = sTot[gg * DK + c0], x1 = sTot[gg * DK + c0 + 1];
+        if (gg < grp) { off0 += x0; off1 += x1; }
+        tot0 += x0; tot1 += x1;
+    }
+    float kb[TPG][2], vb[TPG][2], ke[TPG][2];
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+        const int tl = grp * TPG + i;
+        const float bt = sBeta[tl];
+        const float g0 = lam[i][0] + off0, g1 = lam[i][1] + off1;
+        const float e0 = expf(g0), e1 = expf(g1);
+        const float ei0 = expf(-g0), ei1 = expf(-g1);
+        const float kn0 = kv[i][0] * rk[i], kn1 = kv[i][1] * rk[i];
+        const float qn0 = qv[i][0] * rq[i], qn1 = qv[i][1] * rq[i];
+        st2(sKt + tl * LDR + c0, kn0 * e0, kn1 * e1);
+        st2(sKh + tl * LDR + c0, kn0 * ei0, kn1 * ei1);
+        st2(sQt + tl * LDR + c0, qn0 * e0, qn1 * e1);
+        ke[i][0] = kn0 * expf(tot0 - g0);
+        ke[i][1] = kn1 * expf(tot1 - g1);
+        kb[i][0] = bt * (kn0 * e0);
+        kb[i][1] = bt * (kn1 * e1);
+        vb[i][0] = bt * vv[i][0];
+        vb[i][1] = bt * vv[i][1];
+    }
+    {   // Ke^T rows c0, c0+1: TPG consecutive tokens each
+        E* keT = reinterpret_cast<E*>(card + CL::KET);
+#pragma unroll
+        for (int j = 0; j < TPG; j += 4) {
+            st4(keT + (size_t)c0 * C + grp * TPG + j, f32x4{ke[j][0], ke[j + 1][0], ke[j + 2][0], ke[j + 3][0]});
+            st4(keT + (size_t)(c0 + 1) * C + grp * TPG + j, f32x4{ke[j][1], ke[j + 1][1], ke[j + 2][1], ke[j + 3][1]});
+        }
+        if (grp == 0) {
+            float* gc = reinterpret_cast<float*>(card + CL::GC);
+            *reinterpret_cast<f32x2*>(gc + c0) = f32x2{expf(tot0), expf(tot1)};
+        }
+    }
+    __syncthreads();
+
+    // ---------------- phase B: L = Kt Kh^T, P = Qt Kh^T (lower tiles) ----------------
+    f32x4 acc[5];
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {
+        const int tau = w + 4 * r;
+        const bool isP = tau >= 10;
+        const int id = isP ? tau - 10 : tau;
+        const int ti = (id >= 1) + (id >= 3) + (id >= 6);
+        const int tj = id - ti * (ti + 1) / 2;
+        const E* src = isP ? sQt : sKt;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / KS; ++s)
+            x = M::mma(ld_frag(src, LDR, 16 * ti + n, s * KS, g), ld_frag(sKh, LDR, 16 * tj + n, s * KS, g), x);
+        // masks: L strictly lower (scaled by beta of the row), P lower incl.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * ti + 4 * g + e, col = 16 * tj + n;
+            if (isP) x[e] = (col <= row) ? x[e] : 0.f;
+            else x[e] = (col < row) ? x[e] * sBeta[row] : 0.f;
+        }
+        acc[r] = x;
+    }
+    __syncthreads();
+
+    // ---------------- phase C ----------------
+#pragma unroll
+    for (int i = 0; i < TPG; i += 4) {   // (beta Kt)^T and (beta V)^T, TPG tokens per row
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            st4(sKbT + (c0 + ch) * LDT + grp * TPG + i, f32x4{kb[i][ch], kb[i + 1][ch], kb[i + 2][ch], kb[i + 3][ch]});
+            st4(sVbT + (c0 + ch) * LDT + grp * TPG + i, f32x4{vb[i][ch], vb[i + 1][ch], vb[i + 2][ch], vb[i + 3][ch]});
+        }
+    }
+    {   // Qt -> card (16-byte pieces)
+        constexpr int V16 = 16 / (int)sizeof(E);      // elements per 16 bytes
+        constexpr int PER_ROW = DK / V16;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        char* dst = card + CL::QT;
+        for (int idx = t; idx < C * PER_ROW; idx += kThreads) {
+            const int row = idx / PER_ROW, col = idx % PER_ROW;
+            *reinterpret_cast<u32x4*>(dst + ((size_t)row * DK + col * V16) * sizeof(E)) =
+                *reinterpret_cast<const u32x4*>(sQt + row * LDR + col * V16);
+        }
+    }
+    {   // P -> card: the 10 computed lower tiles, then zeros for the 6 upper tiles
+        E* cp_ = reinterpret_cast<E*>(card + CL::P);
+#pragma unroll
+        for (int r = 0; r < 5; ++r) {
+            const int tau = w + 4 * r;
+            if (tau >= 10) {
+                const int id = tau - 10;
+                const int ti = (id >= 1) + (id >= 3) + (id >= 6);
+                const int tj = id - ti * (ti + 1) / 2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cp_[(16 * ti + 4 * g + e) * C + 16 * tj + n] = from_f32<E>(acc[r][e]);
+            }
+        }
+        for (int idx = t; idx < 6 * 256; idx += kThreads) {
+            const int ut = idx >> 8, el = idx & 255;
+            // upper tiles (ti, tj), tj > ti: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+            const int ti = (ut >= 3) + (ut >= 5);
+            const int tj = ut - (ti == 0 ? 0 : (ti == 1 ? 3 : 5)) + ti + 1;
+            cp_[(16 * ti + (el >> 4)) * C + 16 * tj + (el & 15)] = from_f32<E>(0.f);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {   // diag(beta) L -> sA (fp32; overwrites Qt)
+        const int tau = w + 4 * r;
+        if (tau < 10) {
+            const int ti = (tau >= 1) + (tau >= 3) + (tau >= 6);
+            const int tj = tau - ti * (ti + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sA[(16 * ti + 4 * g + e) * LDA + 16 * tj + n] = acc[r][e];
+        }
+    }
+    __syncthreads();
+
+    // ---------------- phase D: T = (I + A)^-1, in place in sA ----------------
+    {   // D1: diagonal 16x16 blocks by forward substitution; lane n owns column n
+        float x[16];
+        if (g == 0) {
+            const float* Ab = sA + (16 * w) * LDA + 16 * w;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == n) ? 1.f : 0.f;
+#pragma unroll
+                for (int kk = 0; kk < i; ++kk) s -= Ab[i * LDA + kk] * x[kk];
+                x[i] = s;
+            }
+        }
+        __syncthreads();
+        if (g == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sA[(16 * w + i) * LDA + 16 * w + n] = x[i];
+        }
+        __syncthreads();
+    }
+    // D2: block row i: T_ij = -D_i * sum_{kb=j}^{i-1} A_{i,kb} T_{kb,j}; wave j computes T_ij
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+        f32x4 tij = {0.f, 0.f, 0.f, 0.f};
+        if (w < i) {
+            const int j = w;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = j; kb < i; ++kb) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    x = mma_f32(sA[(16 * i + n) * LDA + 16 * kb + 4 * s + g],
+                                sA[(16 * kb + 4 * s + g) * LDA + 16 * j + n], x);
+            }
+            // D_i * X with X taken straight from the accumulator: at step s,
+            // lane group g holds X[4g + s][n], so A supplies D_i[m][4g + s]
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                tij = mma_f32(sA[(16 * i + n) * LDA + 16 * i + 4 * g + s], x[s], tij);
+        }
+        __syncthreads();
+        if (w < i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sA[(16 * i + 4 * g + e) * LDA + 16 * w + n] = -tij[e];
+        }
+        __syncthreads();
+    }
+    // D3: T -> MFMA operand type, zero above the diagonal
+    for (int idx = t; idx < C * C / 4; idx += kThreads) {
+        const int row = idx / (C / 4), col = (idx % (C / 4)) * 4;
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (col + e <= row) ? sA[row * LDA + col + e] : 0.f;
+        st4(sTb + row * LDT + col, x);
+    }
+    __syncthreads();
+
+    // ---------------- phase E: Wk = T (beta Kt), Wv = T (beta V) ----------------
+    constexpr int NTW = NT / 4;   // column tiles per wave
+    f32x4 wk[NTW][4];
+#pragma unroll
+    for (int jt = 0; jt < NTW; ++jt) {
+        const int ni = w * NTW + jt;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xv = {0.f, 0.f, 0.f, 0.f};
+            constexpr int dummy = 0; (void)dummy;
+            const int nks = (16 * (mi + 1) + KS - 1) / KS;
+#pragma unroll
+            for (int s = 0; s < (C / KS); ++s) {
+                if (s < nks) {
+                    const auto af = ld_frag(sTb, LDT, 16 * mi + n, s * KS, g);
+                    xk = M::mma(af, ld_frag(sKbT, LDT, 16 * ni + n, s * KS, g), xk);
+                    xv = M::mma(af, ld_frag(sVbT, LDT, 16 * ni + n, s * KS, g), xv);
+                }
+            }
+            st4(reinterpret_cast<E*>(card + CL::WV) + ((size_t)(ni * 4 + mi) * 64 + lane) * 4, xv);
+            wk[jt][mi] = xk;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < NTW; ++jt)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sWk[(16 * mi + 4 * g + e) * LDR + 16 * (w * NTW + jt) + n] = from_f32<E>(wk[jt][mi][e]);
+    __syncthreads();
+    {
+        constexpr int V16 = 16 / (int)sizeof(E);
+        constexpr int PER_ROW = DK / V16;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        char* dst = card + CL::WK;
+        for (int idx = t; idx < C * PER_ROW; idx += kThreads) {
+            const int row = idx / PER_ROW, col = idx % PER_ROW;
+            *reinterpret_cast<u32x4*>(dst + ((size_t)row * DK + col * V16) * sizeof(E)) =
+                *reinterpret_cast<const u32x4*>(sWk + row * LDR + col * V16);
+        }
+    }
+}
+
+template <typename E, int DK>
+hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t s) {
+    const int64_t blocks = a.B * (int64_t)a.H * a.NC;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((kda_prepare_kernel<E, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t card_bytes(bool bf16, int dk) {
+    if (bf16) return dk == 128 ? Card<__bf16, 128>::BYTES : Card<__bf16, 64>::BYTES;
+    return dk == 128 ? Card<float, 128>::BYTES : Card<float, 64>::BYTES;
+}
+
+hipError_t launch_prepare(bool bf16, int dk, const PrepareArgs& a, hipStream_t s) {
+    if (bf16) return dk == 128 ? launch_prepare_t<__bf16, 128>(a, s) : launch_prepare_t<__bf16, 64>(a, s);
+    return dk == 128 ? launch_prepare_t<float, 128>(a, s) : launch_prepare_t<float, 64>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,138 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) KDA token mixer.
+ *
+ * KDA (Kimi Delta Attention) keeps, per batch row b and head h, a fixed-size
+ * memory S (d_k x d_v, fp32, row = key channel).  Token t updates and reads it:
+ *
+ *   lambda = max(log_alpha_t, log_alpha_min)            per key channel
+ *   S     <- diag(exp(lambda)) S                        channel-wise retention
+ *   kh, qh = k_t / |k_t|, q_t / |q_t|                   (|x| floored at 1e-6)
+ *   u      = beta_t (v_t - S^T kh);   S <- S + kh u^T   delta-rule corrective write
+ *   out_t  = (S^T qh) * sigmoid(g_t)                    full-rank output gate
+ *
+ * Sources: zuoshipin.com/article/18261 §二 (channel-wise forget gate, delta-
+ * rule corrective write, full-rank output gate, per-step retention lower
+ * bound that keeps the parallel form inside bf16 range); devpress.csdn.net K3
+ * article §二 (predict from memory, take the error, write the correction).
+ * The pages print no formula; the exact step order above is the plainest
+ * reading of their words.
+ *
+ * Conventions for every call:
+ *  - Array pointers are DEVICE pointers, C-contiguous and 16-byte aligned;
+ *    beta only needs 4-byte alignment (so one decode step's slice of a
+ *    step-major [T, N, H] array can be passed as is).  Token arrays are
+ *    token-major [B, T, H, d]; states are [B, H, d_k, d_v] fp32.  A segmented sequence [B, n*Ts, H, d] is the same
+ *    memory as [B*n, Ts, H, d], so segments are simply extra batch rows.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous on it; buffers must stay alive until the work completes.
+ *  - The caller owns all memory, including the workspace.  Nothing on the
+ *    path allocates, and the library keeps no mutable global state, so calls
+ *    are reentrant and may run concurrently on different streams.
+ *  - All checks are synchronous and happen before any launch.  Invalid
+ *    arguments return an error and launch nothing.  A failed launch returns
+ *    KDA_ERR_HIP.  No data-dependent checks are made: NaN/Inf propagate.
+ *  - Preconditions that are documented but not checked: log_alpha <= 0 and
+ *    beta in [0, 1] (then every per-token map is a contraction).
+ *  - Supported shapes: d_k == d_v in {64, 128}; chunk == 64; any seqlen >= 0
+ *    (a partial last chunk is padded with identity tokens inside the kernels).
+ *  - log_alpha_min must lie in [-80/chunk, 0): the floor keeps the decay
+ *    folded into one chunk's operands, exp(chunk * |log_alpha_min|), inside
+ *    fp32/bf16 range.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, out-of-range floor */
+    KDA_ERR_UNSUPPORTED = 2,        /* shape or dtype this build does not implement */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} kda_status;
+
+typedef enum {
+    KDA_F32 = 0,                    /* q, k, v, g, out are float32 */
+    KDA_BF16 = 1                    /* q, k, v, g, out are bfloat16 */
+} kda_dtype;
+
+typedef struct {
+    int64_t batch;          /* B (rows; for segments: B * n_seg)                 */
+    int64_t seqlen;         /* T (for segments: the segment length), >= 0        */
+    int32_t heads;          /* H                                                 */
+    int32_t dk, dv;         /* head dims; d_k == d_v in {64, 128}                */
+    int32_t chunk;          /* chunk length C; 64                                */
+    kda_dtype io_dtype;     /* dtype of q, k, v, g and out                       */
+    float log_alpha_min;    /* per-step retention floor, in log space            */
+} kda_problem;
+
+/* Bytes of "update cards" kda_chunk_prepare writes for problem p: one card per
+ * (batch row, head, chunk).  Returns 0 if p is invalid or unsupported. */
+size_t kda_workspace_size(const kda_problem* p);
+
+/* Stage 1 of the chunk method: prepare every chunk's update card in parallel
+ * [zuoshipin.com/article/18261 §四, FlashKDA paragraph: the forget gate,
+ * query/key normalisation, decay and the intra-chunk correction matrix are
+ * prepared per chunk ahead of the ordered stage].
+ *   q, k: [B,T,H,dk] io_dtype;  v: [B,T,H,dv] io_dtype
+ *   log_alpha: [B,T,H,dk] fp32 (the floor is applied here);  beta: [B,T,H] fp32
+ *   workspace: >= kda_workspace_size(p) bytes, written entirely. */
+kda_status kda_chunk_prepare(const kda_problem* p, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2: the ordered state hand-off and the gated read-out (same passage:
+ * only the hand-off and the output read-out stay sequential).
+ *   workspace: the cards of kda_chunk_prepare for the same p
+ *   g: [B,T,H,dv] io_dtype;  out: [B,T,H,dv] io_dtype
+ *   state_in: [B,H,dk,dv] fp32, or NULL for an empty memory
+ *   state_out: [B,H,dk,dv] fp32, or NULL; may equal state_in (in-place resume,
+ *   the KDA state checkpoint of devpress.csdn.net K3 article §十四). */
+kda_status kda_chunk_scan(const kda_problem* p, const void* workspace, size_t workspace_bytes,
+                          const void* g, const float* state_in, void* out, float* state_out,
+                          void* stream);
+
+/* Per-segment summary of the context-parallel scheme [zuoshipin.com/article/
+ * 18261 §三, "KDA 上下文并行" paragraph: each segment reports how it changes an
+ * existing memory and what it builds from an empty one].  For every
+ * (batch row, head) of p, with the cards of kda_chunk_prepare:
+ *   transition: [B,H,dk,dk] fp32 -- A with S_end = A S_start + zero_state
+ *   zero_state: [B,H,dk,dv] fp32 -- the state built from S_start = 0 */
+kda_status kda_segment_summarize(const kda_problem* p, const void* workspace, size_t workspace_bytes,
+                                 float* transition, float* zero_state, void* stream);
+
+/* In-order prefix merge of segment summaries (same paragraph): for each (b, h)
+ *   S(0) = state_init (or 0 if NULL);  seg_state_in[n] = S(n);
+ *   S(n+1) = transition[n] S(n) + zero_state[n];  state_final = S(n_seg).
+ *   transition: [B,n_seg,H,dk,dk]; zero_state, seg_state_in: [B,n_seg,H,dk,dv];
+ *   state_init, state_final: [B,H,dk,dv] (state_final may be NULL).  fp32. */
+kda_status kda_segment_combine(int64_t B, int32_t n_seg, int32_t H, int32_t dk, int32_t dv,
+                               const float* transition, const float* zero_state,
+                               const float* state_init, float* seg_state_in, float* state_final,
+                               void* stream);
+
+/* One decode step for N independent sequences: the fixed-size memory is
+ * updated in place instead of growing a per-token cache [devpress.csdn.net K3
+ * article §十六: KDA keeps a recursive state, not per-token K/V; §十四: state
+ * checkpoints].
+ *   q, k: [N,H,dk]; v, g, out: [N,H,dv] io_dtype;  log_alpha: [N,H,dk] fp32;
+ *   beta: [N,H] fp32;  state: [N,H,dk,dv] fp32, read and written in place. */
+kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype,
+                           float log_alpha_min, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const void* g,
+                           float* state, void* out, void* stream);
+
+/* Static text for a status code. */
+const char* kda_status_string(kda_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
