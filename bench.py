@@ -1,0 +1,233 @@
+"""KDA benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
+
+A step is one chunked prefill (update-card preparation + ordered hand-off
+with the gated read-out) of the long-prefill workload: B=1, T=65,536, H=32,
+d_k=d_v=128, bf16 q/k/v/g/out, fp32 gates and state, chunk 64, synthetic
+inputs (kda_inputs, seed 2), resident in HBM before timing starts.  `value`
+is prefill tokens/s (sequence tokens; all 32 heads).
+
+Also reported on the same JSON line:
+  * per-kernel average durations from HIP events recorded on the launch
+    stream inside the timed region, and the roofline of the dominant kernel
+    (algorithmic bytes per launch / its average duration, against 8 TB/s);
+  * the whole path against the HBM and bf16-MFMA peaks;
+  * the batched decode workload (256 sequences x 32 heads, d=128, 64 steps,
+    fp32 state updated in place): GB/s and fraction of HBM peak;
+  * cpu_baseline: the fp64 oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
+C = 64
+D = 128
+# algorithmic bytes per token-head (bf16 I/O, fp32 log-decay and beta):
+PATH_BYTES = 4 * D * 2 + D * 4 + 4 + D * 2          # q,k,v,g in; log_alpha, beta in; out -> 1,796
+CARD_BYTES = 74240 // C                               # update card per token-head (bf16, d=128) -> 1,160
+PREP_BYTES = 3 * D * 2 + D * 4 + 4 + CARD_BYTES       # q,k,v,log_alpha,beta in; card out -> 2,444
+SCAN_BYTES = CARD_BYTES + D * 2 + D * 2               # card, g in; out -> 1,672
+# algorithmic FLOPs per token-head of the chunk method (triangular C x C products at half):
+FLOP_TOK = 6 * D * D + C * (3 * D + 2 * D) + C * C / 3
+# decode: per (sequence, head) the fp32 state is read and written once, plus the token's inputs/outputs
+DEC_BYTES = 2 * D * D * 4 + (2 * D * 2 + D * 4 + 4 + D * 2 + D * 2) + D * 2
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_91_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, src: str, tokens_heads: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(p)).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_hash") != src:
+        return None
+    return rec["bytes_per_token_head"] * tokens_heads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build measures the single-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import gated_delta_rule_91_amd as kda
+    from kda_inputs import WORKLOADS, workload
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    result = {}
+
+    # ------------------------------------------------------------------ prefill
+    W = WORKLOADS[2]
+    B, T, H = W["B"], W["T"], W["H"]
+    if not args.decode_only:
+        t0 = time.time()
+        inp = workload(2)
+        log(f"[bench] generated prefill inputs in {time.time() - t0:.1f}s")
+        d = kda.to_device(inp, dev)
+        floor = inp.log_alpha_min
+        del inp
+        p = kda.problem(B, T, H, D, D, kda.KDA_BF16, floor)
+        ws = torch.empty(kda.workspace_size(p), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(d["g"])
+        st = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+
+        def step(evs=None):
+            if evs is not None:
+                evs[0].record(stream)
+            kda.chunk_prepare(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], floor, workspace=ws)
+            if evs is not None:
+                evs[1].record(stream)
+            kda.chunk_scan(ws, d["g"], floor, state_in=None, out=out, state_out=st)
+            if evs is not None:
+                evs[2].record(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+        scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        ms = wall * 1e3 / args.steps
+        th = B * T * H
+        log(f"[bench] prefill {ms:.3f} ms/step (prepare {prep_ms:.3f} ms, scan {scan_ms:.3f} ms)")
+        shash = {"kda_prepare_kernel": src_hash("kda_prepare.hip", "kda_common.hpp"),
+                 "kda_scan_kernel": src_hash("kda_scan.hip", "kda_common.hpp")}
+        kern = {"kda_prepare_kernel": (prep_ms, PREP_BYTES), "kda_scan_kernel": (scan_ms, SCAN_BYTES)}
+        dom = max(kern, key=lambda k: kern[k][0])
+        dms, dbytes = kern[dom]
+        achieved = dbytes * th / (dms * 1e-3) / 1e9
+        result.update(
+            metric="KDA prefill tokens/s + % MFMA peak @T=64K,H=32,d=128; decode GB/s % HBM",
+            value=B * T / (ms * 1e-3), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+            ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+            data="synthetic (seeded; q,k unit-normalised, v,g N(0,1), beta=sigmoid(N(0,1)), "
+                 "log_alpha=-softplus(N(-4,1)) floored at log 0.9)",
+            config={"workload": W["name"], "batch": B, "seq_len": T, "heads": H, "d_k": D, "d_v": D,
+                    "chunk": C, "state": "fp32", "parallelism": "single GPU"},
+            roofline={"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_token_head": dbytes,
+                      "avg_launch_ms": dms, "traffic": traffic_for(dom, shash[dom], th)},
+            kernels_ms={"kda_prepare_kernel": prep_ms, "kda_scan_kernel": scan_ms},
+            path={"algorithmic_bytes_per_token_head": PATH_BYTES,
+                  "hbm_GBps": PATH_BYTES * th / (ms * 1e-3) / 1e9,
+                  "hbm_frac": PATH_BYTES * th / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "flop_per_token_head": FLOP_TOK,
+                  "mfma_TFLOPs": FLOP_TOK * th / (ms * 1e-3) / 1e12,
+                  "mfma_frac_bf16": FLOP_TOK * th / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                  "roofline_ceiling_mfma_frac": min(1.0, FLOP_TOK / PATH_BYTES * HBM_PEAK_GBS / 1e3
+                                                    / MFMA_BF16_PEAK_TFLOPS)},
+        )
+        del d, ws, out, st
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ decode
+    if not args.no_decode:
+        Wd = WORKLOADS[4]
+        inp = workload(4)
+        dd = kda.to_device(inp, dev)
+        N, Td = Wd["B"], Wd["T"]
+        sm = {n: dd[n].transpose(0, 1).contiguous() for n in ("q", "k", "v", "g", "log_alpha", "beta")}
+        state = dd["state0"].clone()
+        outd = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+        floor_d = inp.log_alpha_min
+
+        def dstep(t):
+            kda.decode_step(sm["q"][t], sm["k"][t], sm["v"][t], sm["log_alpha"][t], sm["beta"][t], sm["g"][t],
+                            state, floor_d, out=outd)
+
+        for t in range(Td):
+            dstep(t)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for t in range(Td):
+                dstep(t)
+        e1.record()
+        torch.cuda.synchronize()
+        per_step_ms = e0.elapsed_time(e1) / (reps * Td)
+        gbs = DEC_BYTES * N * H / (per_step_ms * 1e-3) / 1e9
+        log(f"[bench] decode {per_step_ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+        result["decode"] = {"workload": Wd["name"], "us_per_step": per_step_ms * 1e3, "GBps": gbs,
+                            "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": DEC_BYTES * N * H,
+                            "tokens_per_s": N / (per_step_ms * 1e-3)}
+        # achievable-bandwidth reference in the same job: a plain device copy
+        x = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            y.copy_(x)
+        e1.record()
+        torch.cuda.synchronize()
+        result["hbm_copy_GBps"] = 2 * x.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del dd, sm, state, x, y
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- cpu baseline
+    if not args.no_cpu_baseline and not args.decode_only:
+        import oracle
+        from kda_inputs import to_f64
+        heads = 8
+        sample = workload(2, H=heads)
+        f = lambda a: to_f64(a, "bf16")
+        args_o = (f(sample.q), f(sample.k), f(sample.v), sample.log_alpha, sample.beta, f(sample.g),
+                  sample.log_alpha_min)
+        nthr = oracle.default_threads()
+        t0 = time.perf_counter()
+        oracle.kda_ref(*args_o, nthreads=nthr)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": T / (dt * H / heads), "unit": "tokens/s", "cores": nthr,
+                                  "kind": "oracle",
+                                  "sample": f"fp64 step recurrence on {heads} of {H} heads x {T} tokens "
+                                            f"({dt:.1f} s), scaled to all {H} heads"}
+        log(f"[bench] oracle {dt:.1f}s on {nthr} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

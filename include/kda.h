@@ -21,8 +21,9 @@
  *  - Array pointers are DEVICE pointers, C-contiguous and 16-byte aligned;
  *    beta only needs 4-byte alignment (so one decode step's slice of a
  *    step-major [T, N, H] array can be passed as is).  Token arrays are
- *    token-major [B, T, H, d]; states are [B, H, d_k, d_v] fp32.  A segmented sequence [B, n*Ts, H, d] is the same
- *    memory as [B*n, Ts, H, d], so segments are simply extra batch rows.
+ *    token-major [B, T, H, d]; states are [B, H, d_k, d_v] fp32.  A
+ *    segmented sequence [B, n*Ts, H, d] is the same memory as
+ *    [B*n, Ts, H, d], so segments are simply extra batch rows.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous on it; buffers must stay alive until the work completes.
  *  - The caller owns all memory, including the workspace.  Nothing on the
