@@ -36,6 +36,22 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// One transpose-reduce exchange over lanes l and l ^ (4*HALF): the lane with
+// that bit clear keeps (and sums) values [0, HALF), the other [HALF, 2*HALF),
+// each sending the half it gives up.  Values end in x[0..HALF).
+template <int HALF>
+__device__ __forceinline__ void tr_halve(float* x, float* y, int lane) {
+    constexpr int m = 4 * HALF;
+    const bool hi = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+        const float sx = hi ? x[j] : x[j + HALF], kx = hi ? x[j + HALF] : x[j];
+        const float sy = hi ? y[j] : y[j + HALF], ky = hi ? y[j + HALF] : y[j];
+        x[j] = kx + __shfl_xor(sx, m);
+        y[j] = ky + __shfl_xor(sy, m);
+    }
+}
+
 template <typename E, int DK>
 struct PrepLds {
     static constexpr int C = kChunk;
@@ -55,7 +71,9 @@ struct PrepLds {
     static constexpr int NG = kThreads / (DK / 2);
     static constexpr size_t TOT = R4 + R4SZ;                    // fp32 [NG][DK]
     static constexpr size_t BETA = TOT + (size_t)NG * DK * 4;   // fp32 [C]
-    static constexpr size_t BYTES = BETA + (size_t)C * 4;
+    static constexpr size_t RQ = BETA + (size_t)C * 4;          // fp32 [C] 1/|q|
+    static constexpr size_t RK = RQ + (size_t)C * 4;            // fp32 [C] 1/|k|
+    static constexpr size_t BYTES = RK + (size_t)C * 4;
 };
 
 template <typename E, int DK>
@@ -81,6 +99,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     E* sWk = reinterpret_cast<E*>(lds + LY::R0);     // phase E: Wk staging
     float* sTot = reinterpret_cast<float*>(lds + LY::TOT);
     float* sBeta = reinterpret_cast<float*>(lds + LY::BETA);
+    float* sRq = reinterpret_cast<float*>(lds + LY::RQ);
+    float* sRk = reinterpret_cast<float*>(lds + LY::RK);
 
     const int t = threadIdx.x;
     const int lane = t & 63, w = t >> 6, g = lane >> 4, n = lane & 15;
@@ -99,31 +119,50 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     const E* q = reinterpret_cast<const E*>(a.q);
     const E* k = reinterpret_cast<const E*>(a.k);
     const E* v = reinterpret_cast<const E*>(a.v);
+    (void)tok0;
 
     // ---------------- phase A ----------------
+    // Log-decay is carried in base-2 units (lambda * log2 e) so every
+    // exponential is a single v_exp_f32; e^-gamma comes from v_rcp_f32.
+    constexpr float kLog2e = 1.4426950408889634f;
     const int cp = t % CP, grp = t / CP, c0 = 2 * cp;
+    // per-workgroup base pointers; per-token offsets stay 32-bit (a chunk of
+    // one head spans at most 64 * H * DK elements)
+    const size_t row0 = ((size_t)b * T + tok0) * H + h;
+    const float* la_b = a.log_alpha + row0 * DK;
+    const E* q_b = q + row0 * DK;
+    const E* k_b = k + row0 * DK;
+    const E* v_b = v + row0 * DK;
+    const uint32_t tstride = (uint32_t)H * DK;
+    const int nvalid = (int)((T - tok0) < C ? (T - tok0) : C);
+    // Loads are unconditional (a padded token re-reads the last valid row and
+    // is zeroed afterwards): a load under a branch would be followed by a
+    // full wait on every outstanding load, serialising the chunk's fetches.
     float lam[TPG][2], qv[TPG][2], kv[TPG][2], vv[TPG][2];
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
-        const int64_t tt = tok0 + grp * TPG + i;
-        if (tt < T) {
-            const size_t row = ((size_t)b * T + tt) * H + h;
-            const f32x2 l2 = *reinterpret_cast<const f32x2*>(a.log_alpha + row * DK + c0);
-            const f32x2 q2 = ld2(q + row * DK + c0), k2 = ld2(k + row * DK + c0), v2 = ld2(v + row * DK + c0);
-            lam[i][0] = fmaxf(l2[0], a.floor_);
-            lam[i][1] = fmaxf(l2[1], a.floor_);
-            qv[i][0] = q2[0]; qv[i][1] = q2[1];
-            kv[i][0] = k2[0]; kv[i][1] = k2[1];
-            vv[i][0] = v2[0]; vv[i][1] = v2[1];
-        } else {   // identity padding: lambda = 0, beta = 0, q = k = v = 0
-            lam[i][0] = lam[i][1] = 0.f;
-            qv[i][0] = qv[i][1] = kv[i][0] = kv[i][1] = vv[i][0] = vv[i][1] = 0.f;
-        }
+        const int tl = grp * TPG + i;
+        const uint32_t off = (uint32_t)(tl < nvalid ? tl : nvalid - 1) * tstride + c0;
+        const f32x2 l2 = *reinterpret_cast<const f32x2*>(la_b + off);
+        const f32x2 q2 = ld2(q_b + off), k2 = ld2(k_b + off), v2 = ld2(v_b + off);
+        lam[i][0] = l2[0]; lam[i][1] = l2[1];
+        qv[i][0] = q2[0]; qv[i][1] = q2[1];
+        kv[i][0] = k2[0]; kv[i][1] = k2[1];
+        vv[i][0] = v2[0]; vv[i][1] = v2[1];
     }
-    if (t < C) {
-        const int64_t tt = tok0 + t;
-        sBeta[t] = (tt < T) ? a.beta[((size_t)b * T + tt) * H + h] : 0.f;
+    float btok = 0.f;
+    if (t < C) btok = a.beta[row0 + (size_t)(t < nvalid ? t : nvalid - 1) * H];
+#pragma unroll
+    for (int i = 0; i < TPG; ++i) {
+        // identity padding: lambda = 0, q = k = v = 0 (and beta = 0 below)
+        const bool ok = grp * TPG + i < nvalid;
+        lam[i][0] = ok ? fmaxf(lam[i][0], a.floor_) * kLog2e : 0.f;
+        lam[i][1] = ok ? fmaxf(lam[i][1], a.floor_) * kLog2e : 0.f;
+        qv[i][0] = ok ? qv[i][0] : 0.f; qv[i][1] = ok ? qv[i][1] : 0.f;
+        kv[i][0] = ok ? kv[i][0] : 0.f; kv[i][1] = ok ? kv[i][1] : 0.f;
+        vv[i][0] = ok ? vv[i][0] : 0.f; vv[i][1] = ok ? vv[i][1] : 0.f;
     }
+    if (t < C) sBeta[t] = (t < nvalid) ? btok : 0.f;
     // inclusive cumulative log-decay inside the group
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
@@ -133,19 +172,28 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     }
     sTot[grp * DK + c0] = run0;
     sTot[grp * DK + c0 + 1] = run1;
-    // q/k norms: reduce over the CP lanes that share this token group
-    float rq[TPG], rk[TPG];
+    {   // q/k squared norms of the group's TPG tokens, summed over its CP lanes.
+        // Transpose-reduce: each exchange halves the number of values a lane
+        // carries, so lane l ends with the full sum of token (l >> 2) % TPG.
+        float sq[TPG], sk[TPG];
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-        float sq = qv[i][0] * qv[i][0] + qv[i][1] * qv[i][1];
-        float sk = kv[i][0] * kv[i][0] + kv[i][1] * kv[i][1];
-#pragma unroll
-        for (int off = 1; off < CP; off <<= 1) {
-            sq += __shfl_xor(sq, off);
-            sk += __shfl_xor(sk, off);
+        for (int i = 0; i < TPG; ++i) {
+            sq[i] = qv[i][0] * qv[i][0] + qv[i][1] * qv[i][1];
+            sk[i] = kv[i][0] * kv[i][0] + kv[i][1] * kv[i][1];
         }
-        rq[i] = 1.0f / fmaxf(sqrtf(sq), 1e-6f);
-        rk[i] = 1.0f / fmaxf(sqrtf(sk), 1e-6f);
+        if constexpr (TPG >= 16) tr_halve<8>(sq, sk, lane);
+        if constexpr (TPG >= 8) tr_halve<4>(sq, sk, lane);
+        tr_halve<2>(sq, sk, lane);
+        tr_halve<1>(sq, sk, lane);
+        sq[0] += __shfl_xor(sq[0], 2);
+        sk[0] += __shfl_xor(sk[0], 2);
+        sq[0] += __shfl_xor(sq[0], 1);
+        sk[0] += __shfl_xor(sk[0], 1);
+        if ((lane & 3) == 0) {
+            const int tl = grp * TPG + ((lane >> 2) & (TPG - 1));
+            sRq[tl] = 1.0f / fmaxf(sqrtf(sq[0]), 1e-6f);
+            sRk[tl] = 1.0f / fmaxf(sqrtf(sk[0]), 1e-6f);
+        }
     }
     __syncthreads();
 
@@ -160,17 +208,17 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
         const int tl = grp * TPG + i;
-        const float bt = sBeta[tl];
+        const float bt = sBeta[tl], rq = sRq[tl], rk = sRk[tl];
         const float g0 = lam[i][0] + off0, g1 = lam[i][1] + off1;
-        const float e0 = expf(g0), e1 = expf(g1);
-        const float ei0 = expf(-g0), ei1 = expf(-g1);
-        const float kn0 = kv[i][0] * rk[i], kn1 = kv[i][1] * rk[i];
-        const float qn0 = qv[i][0] * rq[i], qn1 = qv[i][1] * rq[i];
+        const float e0 = __builtin_amdgcn_exp2f(g0), e1 = __builtin_amdgcn_exp2f(g1);
+        const float ei0 = __builtin_amdgcn_rcpf(e0), ei1 = __builtin_amdgcn_rcpf(e1);
+        const float kn0 = kv[i][0] * rk, kn1 = kv[i][1] * rk;
+        const float qn0 = qv[i][0] * rq, qn1 = qv[i][1] * rq;
         st2(sKt + tl * LDR + c0, kn0 * e0, kn1 * e1);
         st2(sKh + tl * LDR + c0, kn0 * ei0, kn1 * ei1);
         st2(sQt + tl * LDR + c0, qn0 * e0, qn1 * e1);
-        ke[i][0] = kn0 * expf(tot0 - g0);
-        ke[i][1] = kn1 * expf(tot1 - g1);
+        ke[i][0] = kn0 * __builtin_amdgcn_exp2f(tot0 - g0);
+        ke[i][1] = kn1 * __builtin_amdgcn_exp2f(tot1 - g1);
         kb[i][0] = bt * (kn0 * e0);
         kb[i][1] = bt * (kn1 * e1);
         vb[i][0] = bt * vv[i][0];
@@ -185,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
         }
         if (grp == 0) {
             float* gc = reinterpret_cast<float*>(card + CL::GC);
-            *reinterpret_cast<f32x2*>(gc + c0) = f32x2{expf(tot0), expf(tot1)};
+            *reinterpret_cast<f32x2*>(gc + c0) = f32x2{__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1)};
         }
     }
     __syncthreads();

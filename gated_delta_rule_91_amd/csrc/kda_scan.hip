@@ -15,9 +15,12 @@
 // state slice (d_k x 16, fp32) lives in accumulator registers for the whole
 // sequence.  Four waves share a chain: wave w owns U/O rows 16w..16w+15 and
 // state rows w*d_k/4 .. (w+1)*d_k/4 - 1.  U and the operand copy of S cross
-// waves through LDS (two barriers per chunk); the chunk's card operands are
-// prefetched from global memory one chunk ahead, straight into registers in
-// MFMA operand layout.
+// waves through LDS (two barriers per chunk); the card operands and the gate
+// values are prefetched from global memory four chunks ahead, straight into
+// registers in MFMA operand layout (a register ring, so the dependent chunk
+// loop never waits on memory latency).  Every global load is unconditional:
+// the load counter retires in order, so a load under a branch makes the
+// compiler wait for ALL outstanding loads, which would drain the ring.
 //
 // Summary mode runs the same hand-off on the augmented state [Bz | A] from
 // [0 | I]: the first d_v/16 chains carry value columns (from 0), the next
@@ -37,23 +40,45 @@ namespace {
 
 constexpr int kXcds = 8;
 
+// Four consecutive elements kept as loaded; widened to fp32 only where used,
+// so no conversion sits right behind its load.
+template <typename E> struct Raw4 { typedef f32x4 type; };
+template <> struct Raw4<__bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 widen4(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+__device__ __forceinline__ f32x4 widen4(f32x4 x) { return x; }
+
 template <typename E, int DK>
 struct ChunkOps {
     using M = MM<E>;
     static constexpr int NKD = DK / M::KS;      // k-steps over d_k
     static constexpr int NKC = kChunk / M::KS;  // k-steps over the chunk's tokens
     static constexpr int MTS = DK / 64;         // 16-row state tiles per wave
-    typename M::frag wk[NKD];                   // -Wk rows 16w..16w+15
+    typename M::frag wk[NKD];                   // Wk rows 16w..16w+15
     typename M::frag qt[NKD];                   // Qt rows 16w..16w+15
     typename M::frag ke[MTS][NKC];              // Ke^T rows of this wave's state tiles
     typename M::frag p[NKC];                    // P rows 16w..16w+15
-    f32x4 wv;                                   // Wv tile (accumulator order)
+    typename Raw4<E>::type wv;                  // Wv tile (accumulator order), raw
     f32x4 gc[MTS];                              // e^gamma_C for the lane's state rows
+    uint32_t graw[4];                           // output-gate pre-activations, rows 4g..4g+3 (raw bits)
 };
+
+// Gate values are fetched as aligned 32-bit words (for bf16: the pair of
+// columns holding this lane's column) -- plain dword loads keep the load
+// counter bookkeeping exact -- and decoded at the point of use.
+__device__ __forceinline__ uint32_t gate_load(const __bf16* p, int n) {
+    return *reinterpret_cast<const uint32_t*>(p - (n & 1));
+}
+__device__ __forceinline__ uint32_t gate_load(const float* p, int) { return *reinterpret_cast<const uint32_t*>(p); }
+template <typename E> __device__ __forceinline__ float gate_value(uint32_t x, int n);
+template <> __device__ __forceinline__ float gate_value<__bf16>(uint32_t x, int n) {
+    return __uint_as_float((n & 1) ? (x & 0xffff0000u) : (x << 16));
+}
+template <> __device__ __forceinline__ float gate_value<float>(uint32_t x, int) { return __uint_as_float(x); }
 
 template <typename E, int DK, bool SUMMARY>
 __device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, int w, int g, int n, int lane,
-                                         int tile, bool vcols) {
+                                         int tile, bool vcols, const E* grow, int64_t t0, int64_t T,
+                                         size_t row_stride) {
     using M = MM<E>;
     using CL = Card<E, DK>;
     using O = ChunkOps<E, DK>;
@@ -61,7 +86,7 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, i
     const E* wk = reinterpret_cast<const E*>(card + CL::WK);
     const E* ket = reinterpret_cast<const E*>(card + CL::KET);
 #pragma unroll
-    for (int s = 0; s < O::NKD; ++s) o.wk[s] = M::neg(ld_frag(wk, DK, 16 * w + n, s * KS, g));
+    for (int s = 0; s < O::NKD; ++s) o.wk[s] = ld_frag(wk, DK, 16 * w + n, s * KS, g);
 #pragma unroll
     for (int mt = 0; mt < O::MTS; ++mt)
 #pragma unroll
@@ -71,10 +96,10 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, i
     for (int mt = 0; mt < O::MTS; ++mt)
         o.gc[mt] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(card + CL::GC) +
                                                    (DK / 4) * w + 16 * mt + 4 * g);
-    if (vcols)
-        o.wv = ld4(reinterpret_cast<const E*>(card + CL::WV) + ((size_t)(tile * 4 + w) * 64 + lane) * 4);
-    else
-        o.wv = f32x4{0.f, 0.f, 0.f, 0.f};
+    // unconditional loads only (see the note in the kernel): transition
+    // columns read tile 0 and discard it
+    o.wv = *reinterpret_cast<const typename Raw4<E>::type*>(
+        reinterpret_cast<const E*>(card + CL::WV) + ((size_t)((vcols ? tile : 0) * 4 + w) * 64 + lane) * 4);
     if (!SUMMARY) {
         const E* qt = reinterpret_cast<const E*>(card + CL::QT);
         const E* p = reinterpret_cast<const E*>(card + CL::P);
@@ -82,6 +107,13 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, i
         for (int s = 0; s < O::NKD; ++s) o.qt[s] = ld_frag(qt, DK, 16 * w + n, s * KS, g);
 #pragma unroll
         for (int s = 0; s < O::NKC; ++s) o.p[s] = ld_frag(p, kChunk, 16 * w + n, s * KS, g);
+        // gate rows t0 + 4g + e of this wave's 16 tokens (grow already points
+        // at column col0 + n); rows past the end re-read the last token
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t tt = t0 + 4 * g + e;
+            o.graw[e] = gate_load(grow + (size_t)(tt < T ? tt : T - 1) * row_stride, n);
+        }
     }
 }
 
@@ -136,38 +168,30 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, S[mt]);
 
     const char* cards = a.ws + (size_t)bh * NC * CL::BYTES;
-    const E* gin = reinterpret_cast<const E*>(a.g);
-    E* out = reinterpret_cast<E*>(a.out);
+    const size_t rs = (size_t)H * DK;                                   // elements between tokens
+    const size_t lane_col = ((size_t)b * a.T * H + h) * DK + col0 + n;  // token 0, this lane's column
+    const E* grow = reinterpret_cast<const E*>(a.g) + lane_col;
+    E* orow = reinterpret_cast<E*>(a.out) + lane_col;
 
-    O cur;
-    if (NC > 0) load_ops<E, DK, SUMMARY>(cur, cards, w, g, n, lane, tile, vcols);
-    __syncthreads();
+    // prefetches past the last chunk re-read the last card (never used), so
+    // the steady-state loop has no branches around its loads
+    auto load = [&](O& o, int c) {
+        const int cc = c < NC ? c : NC - 1;
+        load_ops<E, DK, SUMMARY>(o, cards + (size_t)cc * CL::BYTES, w, g, n, lane, tile, vcols, grow,
+                                 (int64_t)cc * C + 16 * w, a.T, rs);
+    };
 
-    for (int c = 0; c < NC; ++c) {
-        O nxt;
-        const bool more = c + 1 < NC;
-        if (more) load_ops<E, DK, SUMMARY>(nxt, cards + (size_t)(c + 1) * CL::BYTES, w, g, n, lane, tile, vcols);
-
-        // gate values for this wave's 16 output rows (issued early)
-        const int64_t tbase = (int64_t)c * C + 16 * w + 4 * g;
-        float gv[4];
-        if (!SUMMARY) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t tt = tbase + e;
-                gv[e] = (tt < a.T) ? to_f32(gin[(((size_t)b * a.T + tt) * H + h) * DK + col0 + n]) : 0.f;
-            }
-        }
-
+    auto step = [&](const O& cur, int c) {
         // S operand (B fragments) from the shared copy
         typename M::frag sb[O::NKD];
 #pragma unroll
         for (int s = 0; s < O::NKD; ++s) sb[s] = ld_frag(sS, LDS_S, n, s * KS, g);
 
-        // U rows 16w..16w+15 = Wv - Wk S
-        f32x4 u = cur.wv;
+        // U rows 16w..16w+15 = Wv - Wk S = -((-Wv) + Wk S)
+        f32x4 u = vcols ? -widen4(cur.wv) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < O::NKD; ++s) u = M::mma(cur.wk[s], sb[s], u);
+        u = -u;
         st4(sU + n * LDS_U + 16 * w + 4 * g, u);
         __syncthreads();
 
@@ -191,18 +215,48 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < O::NKD; ++s) o = M::mma(cur.qt[s], sb[s], o);
+            // P is zero above the diagonal, so the full k range is exact
 #pragma unroll
-            for (int s = 0; s < O::NKC; ++s)
-                if (s * KS < 16 * (w + 1)) o = M::mma(cur.p[s], ub[s], o);
+            for (int s = 0; s < O::NKC; ++s) o = M::mma(cur.p[s], ub[s], o);
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = o[e] * sigmoidf_(gate_value<E>(cur.graw[e], n));
+            // keep the gate math out of the store branch below: inside a branch
+            // the compiler would wait for every outstanding load first
+            asm volatile("" ::"v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t tt = tbase + e;
-                if (tt < a.T)
-                    out[(((size_t)b * a.T + tt) * H + h) * DK + col0 + n] = from_f32<E>(o[e] * sigmoidf_(gv[e]));
+                const int64_t tt = (int64_t)c * C + 16 * w + 4 * g + e;
+                if (tt < a.T) orow[(size_t)tt * rs] = from_f32<E>(y[e]);
             }
         }
         __syncthreads();
-        if (more) cur = nxt;
+    };
+
+    // four chunks of operands in flight: chunk c + 4 is requested as soon as
+    // chunk c's registers are free.  The loop body is branch-free so the
+    // load-counter waits stay exact; up to three chunks finish in the tail.
+    if (NC > 0) {
+        O o0, o1, o2, o3;
+        load(o0, 0);
+        load(o1, 1);
+        load(o2, 2);
+        load(o3, 3);
+        __syncthreads();
+        int c = 0;
+        for (; c + 4 <= NC; c += 4) {
+            step(o0, c);
+            load(o0, c + 4);
+            step(o1, c + 1);
+            load(o1, c + 5);
+            step(o2, c + 2);
+            load(o2, c + 6);
+            step(o3, c + 3);
+            load(o3, c + 7);
+        }
+        if (c < NC) step(o0, c);
+        if (c + 1 < NC) step(o1, c + 1);
+        if (c + 2 < NC) step(o2, c + 2);
     }
 
     // ---- final state slice ----
