@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures the single-GPU path "
@@ -89,6 +91,15 @@ def main():
     torch.cuda.set_device(dev)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     result = {}
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 18   # float32 elements
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}), flush=True)
+        return
 
     # ------------------------------------------------------------------ prefill
     W = WORKLOADS[2]

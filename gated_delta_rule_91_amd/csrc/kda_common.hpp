@@ -94,15 +94,23 @@ __device__ __forceinline__ void st2(__bf16* p, float a, float b) {
 }
 __device__ __forceinline__ void st2(float* p, float a, float b) { *reinterpret_cast<f32x2*>(p) = f32x2{a, b}; }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)) with the hardware exp2 and reciprocal
+// (about 1 ulp each); saturates cleanly to 0 and 1
+__device__ __forceinline__ float sigmoidf_(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
 
 // ---- update card --------------------------------------------------------------
 // One card per (batch row, head, chunk), for chunk length C = 64 and
 // d_k = d_v = DK.  E is the operand type of the ordered stage (bf16 or fp32).
-//   Wk  [C][DK]  row-major   Wk = T diag(beta) Kt         (A operand of U = Wv - Wk S)
-//   Qt  [C][DK]  row-major   q^ * e^gamma                  (A operand of O = Qt S + P U)
-//   KeT [DK][C]  row-major   (k^ * e^(gamma_C - gamma))^T  (A operand of S' = G S + Ke^T U)
-//   P   [C][C]   row-major   lower_incl(Qt Kh^T)           (A operand of P U)
+//   Wk  [C x DK]   Wk = T diag(beta) Kt          (A operand of U = Wv - Wk S)
+//   Qt  [C x DK]   q^ * e^gamma                   (A operand of O = Qt S + P U)
+//   KeT [DK x C]   (k^ * e^(gamma_C - gamma))^T   (A operand of S' = G S + Ke^T U)
+//   P   [C x C]    lower_incl(Qt Kh^T)            (A operand of P U)
+// are stored in MFMA A-fragment order: the matrix is cut into blocks of 16
+// rows x KS columns, blocks row-block-major, and inside a block lane l's
+// fragment (row l % 16, columns KF*(l/16) .. +KF-1) sits at l * KF elements.
+// One wave-wide fragment load is then a single contiguous 64*KF-element run.
 //   Wv  [DK/16][C/16][64][4] in accumulator order: the 16x16 tile (token tile
 //       mi, column tile ni) sits at ((ni*4 + mi)*64 + lane)*4, lane holding
 //       rows 4g..4g+3 of column n -- exactly the C operand of U's MFMA.
@@ -118,5 +126,12 @@ struct Card {
     static constexpr size_t GC = WV + (size_t)C * DK * sizeof(E);
     static constexpr size_t BYTES = ((GC + (size_t)DK * sizeof(float)) + 255) / 256 * 256;
 };
+
+// Element index of (row, k) of an A operand with K columns in fragment order.
+template <typename E>
+__host__ __device__ constexpr int frag_index(int row, int k, int K) {
+    return (((row >> 4) * (K / MM<E>::KS) + k / MM<E>::KS) * 64 +
+            ((k % MM<E>::KS) / MM<E>::KF) * 16 + (row & 15)) * MM<E>::KF + (k % MM<E>::KF);
+}
 
 }  // namespace kda

@@ -24,7 +24,8 @@
 //   D  T by blocked substitution in fp32: 16x16 diagonal blocks by forward
 //      substitution, off-diagonal blocks with fp32 MFMA
 //   E  Wk and Wv on MFMA (block-lower-triangular T); Wv to the card in
-//      accumulator order, Wk through LDS to the card row-major
+//      accumulator order, Wk through LDS to the card in fragment order
+// Qt, Ke^T, P and Wk leave in MFMA A-fragment order (Card, kda_common.hpp).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -49,6 +50,29 @@ __device__ __forceinline__ void tr_halve(float* x, float* y, int lane) {
         const float sy = hi ? y[j] : y[j + HALF], ky = hi ? y[j + HALF] : y[j];
         x[j] = kx + __shfl_xor(sx, m);
         y[j] = ky + __shfl_xor(sy, m);
+    }
+}
+
+// Copy an R x K row-major LDS matrix (leading dimension ld) to global
+// memory in MFMA A-fragment order (see Card in kda_common.hpp).
+template <typename E, int R, int K>
+__device__ __forceinline__ void store_frag_order(char* dst, const E* src, int ld, int t) {
+    constexpr int KF = MM<E>::KF, KS = MM<E>::KS;
+    if constexpr (KF == 8) {   // a lane fragment is one 16-byte run of a source row
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        for (int idx = t; idx < R * K / 8; idx += kThreads) {
+            const int blk = idx >> 6, lane = idx & 63;
+            const int row = 16 * (blk / (K / KS)) + (lane & 15);
+            const int k = (blk % (K / KS)) * KS + (lane >> 4) * KF;
+            *reinterpret_cast<u32x4*>(dst + (size_t)idx * 16) = *reinterpret_cast<const u32x4*>(src + row * ld + k);
+        }
+    } else {
+        for (int idx = t; idx < R * K; idx += kThreads) {
+            const int blk = idx >> 6, lane = idx & 63;
+            const int row = 16 * (blk / (K / KS)) + (lane & 15);
+            const int k = (blk % (K / KS)) * KS + (lane >> 4);
+            reinterpret_cast<E*>(dst)[idx] = src[row * ld + k];
+        }
     }
 }
 
@@ -224,12 +248,23 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
         vb[i][0] = bt * vv[i][0];
         vb[i][1] = bt * vv[i][1];
     }
-    {   // Ke^T rows c0, c0+1: TPG consecutive tokens each
+    {   // Ke^T rows c0, c0+1 (key channels), columns = this group's TPG tokens,
+        // written in fragment order
         E* keT = reinterpret_cast<E*>(card + CL::KET);
 #pragma unroll
-        for (int j = 0; j < TPG; j += 4) {
-            st4(keT + (size_t)c0 * C + grp * TPG + j, f32x4{ke[j][0], ke[j + 1][0], ke[j + 2][0], ke[j + 3][0]});
-            st4(keT + (size_t)(c0 + 1) * C + grp * TPG + j, f32x4{ke[j][1], ke[j + 1][1], ke[j + 2][1], ke[j + 3][1]});
+        for (int ch = 0; ch < 2; ++ch) {
+            if constexpr (M::KF == 8) {
+#pragma unroll
+                for (int j = 0; j < TPG; j += 8) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = (__bf16)ke[j + e][ch];
+                    *reinterpret_cast<bf16x8*>(keT + frag_index<E>(c0 + ch, grp * TPG + j, C)) = x;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < TPG; ++j) keT[frag_index<E>(c0 + ch, grp * TPG + j, C)] = from_f32<E>(ke[j][ch]);
+            }
         }
         if (grp == 0) {
             float* gc = reinterpret_cast<float*>(card + CL::GC);
@@ -272,17 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
             st4(sVbT + (c0 + ch) * LDT + grp * TPG + i, f32x4{vb[i][ch], vb[i + 1][ch], vb[i + 2][ch], vb[i + 3][ch]});
         }
     }
-    {   // Qt -> card (16-byte pieces)
-        constexpr int V16 = 16 / (int)sizeof(E);      // elements per 16 bytes
-        constexpr int PER_ROW = DK / V16;
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        char* dst = card + CL::QT;
-        for (int idx = t; idx < C * PER_ROW; idx += kThreads) {
-            const int row = idx / PER_ROW, col = idx % PER_ROW;
-            *reinterpret_cast<u32x4*>(dst + ((size_t)row * DK + col * V16) * sizeof(E)) =
-                *reinterpret_cast<const u32x4*>(sQt + row * LDR + col * V16);
-        }
-    }
+    store_frag_order<E, C, DK>(card + CL::QT, sQt, LDR, t);   // Qt -> card
     {   // P -> card: the 10 computed lower tiles, then zeros for the 6 upper tiles
         E* cp_ = reinterpret_cast<E*>(card + CL::P);
 #pragma unroll
@@ -294,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
                 const int tj = id - ti * (ti + 1) / 2;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    cp_[(16 * ti + 4 * g + e) * C + 16 * tj + n] = from_f32<E>(acc[r][e]);
+                    cp_[frag_index<E>(16 * ti + 4 * g + e, 16 * tj + n, C)] = from_f32<E>(acc[r][e]);
             }
         }
         for (int idx = t; idx < 6 * 256; idx += kThreads) {
@@ -302,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
             // upper tiles (ti, tj), tj > ti: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
             const int ti = (ut >= 3) + (ut >= 5);
             const int tj = ut - (ti == 0 ? 0 : (ti == 1 ? 3 : 5)) + ti + 1;
-            cp_[(16 * ti + (el >> 4)) * C + 16 * tj + (el & 15)] = from_f32<E>(0.f);
+            cp_[frag_index<E>(16 * ti + (el >> 4), 16 * tj + (el & 15), C)] = from_f32<E>(0.f);
         }
     }
     __syncthreads();
@@ -406,17 +431,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
             for (int e = 0; e < 4; ++e)
                 sWk[(16 * mi + 4 * g + e) * LDR + 16 * (w * NTW + jt) + n] = from_f32<E>(wk[jt][mi][e]);
     __syncthreads();
-    {
-        constexpr int V16 = 16 / (int)sizeof(E);
-        constexpr int PER_ROW = DK / V16;
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        char* dst = card + CL::WK;
-        for (int idx = t; idx < C * PER_ROW; idx += kThreads) {
-            const int row = idx / PER_ROW, col = idx % PER_ROW;
-            *reinterpret_cast<u32x4*>(dst + ((size_t)row * DK + col * V16) * sizeof(E)) =
-                *reinterpret_cast<const u32x4*>(sWk + row * LDR + col * V16);
-        }
-    }
+    store_frag_order<E, C, DK>(card + CL::WK, sWk, LDR, t);   // Wk -> card
 }
 
 template <typename E, int DK>

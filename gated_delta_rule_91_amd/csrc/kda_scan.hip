@@ -65,54 +65,77 @@ struct ChunkOps {
 // Gate values are fetched as aligned 32-bit words (for bf16: the pair of
 // columns holding this lane's column) -- plain dword loads keep the load
 // counter bookkeeping exact -- and decoded at the point of use.
-__device__ __forceinline__ uint32_t gate_load(const __bf16* p, int n) {
-    return *reinterpret_cast<const uint32_t*>(p - (n & 1));
-}
-__device__ __forceinline__ uint32_t gate_load(const float* p, int) { return *reinterpret_cast<const uint32_t*>(p); }
 template <typename E> __device__ __forceinline__ float gate_value(uint32_t x, int n);
 template <> __device__ __forceinline__ float gate_value<__bf16>(uint32_t x, int n) {
     return __uint_as_float((n & 1) ? (x & 0xffff0000u) : (x << 16));
 }
 template <> __device__ __forceinline__ float gate_value<float>(uint32_t x, int) { return __uint_as_float(x); }
 
+// Byte offsets of this lane's operand fragments inside a card: the same for
+// every chunk, so each load is (uniform card base) + (32-bit lane offset) +
+// (immediate), which the compiler issues in the scalar-base form.
+template <typename E, int DK>
+struct LaneOff {
+    static constexpr int MTS = DK / 64;
+    uint32_t wk, qt, p, wv;
+    uint32_t ke[MTS], gc[MTS];
+    uint32_t gcol;   // byte offset of the (aligned) gate word for this lane's column
+    int grow;        // this lane's first gate/output row inside the chunk (16w + 4g)
+
+    __device__ LaneOff(int w, int g, int n, int lane, int tile, bool vcols) {
+        using M = MM<E>;
+        using CL = Card<E, DK>;
+        constexpr int FB = M::KF * (int)sizeof(E);          // bytes of one lane fragment
+        constexpr int NKD = DK / M::KS, NKC = kChunk / M::KS, SZ = (int)sizeof(E);
+        // A operands are in fragment order: block (row block, k step) is 64
+        // consecutive lane fragments
+        wk = (uint32_t)(CL::WK + (w * NKD * 64 + lane) * FB);
+        qt = (uint32_t)(CL::QT + (w * NKD * 64 + lane) * FB);
+        p = (uint32_t)(CL::P + (w * NKC * 64 + lane) * FB);
+        wv = (uint32_t)(CL::WV + (((vcols ? tile : 0) * 4 + w) * 64 + lane) * 4 * SZ);
+#pragma unroll
+        for (int mt = 0; mt < MTS; ++mt) {
+            ke[mt] = (uint32_t)(CL::KET + ((((DK / 64) * w + mt) * NKC) * 64 + lane) * FB);
+            gc[mt] = (uint32_t)(CL::GC + ((DK / 4) * w + 16 * mt + 4 * g) * 4);
+        }
+        gcol = (uint32_t)((SZ == 2 ? (n & ~1) : n) * SZ);
+        grow = 16 * w + 4 * g;
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ T ldc(const char* base, uint32_t off) {
+    return *reinterpret_cast<const T*>(base + off);
+}
+
+// card: this chunk's card (uniform); gbase: the chunk's first token row of g
+// at column col0 (uniform); rsb: bytes between tokens; nvalid: tokens of
+// this chunk inside the sequence (rows past it re-read the last one)
 template <typename E, int DK, bool SUMMARY>
-__device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, int w, int g, int n, int lane,
-                                         int tile, bool vcols, const E* grow, int64_t t0, int64_t T,
-                                         size_t row_stride) {
+__device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, const LaneOff<E, DK>& lo,
+                                         const char* gbase, uint32_t rsb, int nvalid) {
     using M = MM<E>;
-    using CL = Card<E, DK>;
     using O = ChunkOps<E, DK>;
-    constexpr int KS = M::KS;
-    const E* wk = reinterpret_cast<const E*>(card + CL::WK);
-    const E* ket = reinterpret_cast<const E*>(card + CL::KET);
+    typedef typename M::frag F;
+    constexpr int KSB = 64 * M::KF * (int)sizeof(E);   // bytes per fragment block (one k-step)
 #pragma unroll
-    for (int s = 0; s < O::NKD; ++s) o.wk[s] = ld_frag(wk, DK, 16 * w + n, s * KS, g);
-#pragma unroll
-    for (int mt = 0; mt < O::MTS; ++mt)
-#pragma unroll
-        for (int s = 0; s < O::NKC; ++s)
-            o.ke[mt][s] = ld_frag(ket, kChunk, (DK / 4) * w + 16 * mt + n, s * KS, g);
+    for (int s = 0; s < O::NKD; ++s) o.wk[s] = ldc<F>(card, lo.wk + s * KSB);
 #pragma unroll
     for (int mt = 0; mt < O::MTS; ++mt)
-        o.gc[mt] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(card + CL::GC) +
-                                                   (DK / 4) * w + 16 * mt + 4 * g);
-    // unconditional loads only (see the note in the kernel): transition
-    // columns read tile 0 and discard it
-    o.wv = *reinterpret_cast<const typename Raw4<E>::type*>(
-        reinterpret_cast<const E*>(card + CL::WV) + ((size_t)((vcols ? tile : 0) * 4 + w) * 64 + lane) * 4);
+#pragma unroll
+        for (int s = 0; s < O::NKC; ++s) o.ke[mt][s] = ldc<F>(card, lo.ke[mt] + s * KSB);
+#pragma unroll
+    for (int mt = 0; mt < O::MTS; ++mt) o.gc[mt] = ldc<f32x4>(card, lo.gc[mt]);
+    o.wv = ldc<typename Raw4<E>::type>(card, lo.wv);
     if (!SUMMARY) {
-        const E* qt = reinterpret_cast<const E*>(card + CL::QT);
-        const E* p = reinterpret_cast<const E*>(card + CL::P);
 #pragma unroll
-        for (int s = 0; s < O::NKD; ++s) o.qt[s] = ld_frag(qt, DK, 16 * w + n, s * KS, g);
+        for (int s = 0; s < O::NKD; ++s) o.qt[s] = ldc<F>(card, lo.qt + s * KSB);
 #pragma unroll
-        for (int s = 0; s < O::NKC; ++s) o.p[s] = ld_frag(p, kChunk, 16 * w + n, s * KS, g);
-        // gate rows t0 + 4g + e of this wave's 16 tokens (grow already points
-        // at column col0 + n); rows past the end re-read the last token
+        for (int s = 0; s < O::NKC; ++s) o.p[s] = ldc<F>(card, lo.p + s * KSB);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int64_t tt = t0 + 4 * g + e;
-            o.graw[e] = gate_load(grow + (size_t)(tt < T ? tt : T - 1) * row_stride, n);
+            const int r = lo.grow + e < nvalid ? lo.grow + e : nvalid - 1;
+            o.graw[e] = ldc<uint32_t>(gbase, (uint32_t)r * rsb + lo.gcol);
         }
     }
 }
@@ -168,17 +191,21 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, S[mt]);
 
     const char* cards = a.ws + (size_t)bh * NC * CL::BYTES;
-    const size_t rs = (size_t)H * DK;                                   // elements between tokens
-    const size_t lane_col = ((size_t)b * a.T * H + h) * DK + col0 + n;  // token 0, this lane's column
-    const E* grow = reinterpret_cast<const E*>(a.g) + lane_col;
-    E* orow = reinterpret_cast<E*>(a.out) + lane_col;
+    const LaneOff<E, DK> lo(w, g, n, lane, tile, vcols);
+    const uint32_t rsb = (uint32_t)(H * DK * (int)sizeof(E));              // bytes between tokens
+    // first token row of this (b, h) at column col0, as bytes, for g and out
+    const size_t head0 = (((size_t)b * a.T * H + h) * DK + col0) * sizeof(E);
+    const char* gseq = reinterpret_cast<const char*>(a.g) + head0;
+    char* oseq = reinterpret_cast<char*>(a.out) + head0;
+    const uint32_t ocol = (uint32_t)(n * (int)sizeof(E));
 
     // prefetches past the last chunk re-read the last card (never used), so
     // the steady-state loop has no branches around its loads
     auto load = [&](O& o, int c) {
         const int cc = c < NC ? c : NC - 1;
-        load_ops<E, DK, SUMMARY>(o, cards + (size_t)cc * CL::BYTES, w, g, n, lane, tile, vcols, grow,
-                                 (int64_t)cc * C + 16 * w, a.T, rs);
+        const int64_t t0 = (int64_t)cc * C;
+        const int nvalid = (int)(a.T - t0 < C ? a.T - t0 : C);
+        load_ops<E, DK, SUMMARY>(o, cards + (size_t)cc * CL::BYTES, lo, gseq + (size_t)t0 * rsb, rsb, nvalid);
     };
 
     auto step = [&](const O& cur, int c) {
@@ -224,10 +251,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
             // keep the gate math out of the store branch below: inside a branch
             // the compiler would wait for every outstanding load first
             asm volatile("" ::"v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
+            char* ochunk = oseq + (size_t)c * C * rsb;
+            const int nvalid = (int)(a.T - (int64_t)c * C < C ? a.T - (int64_t)c * C : C);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t tt = (int64_t)c * C + 16 * w + 4 * g + e;
-                if (tt < a.T) orow[(size_t)tt * rs] = from_f32<E>(y[e]);
+                const int r = lo.grow + e;
+                if (r < nvalid) *reinterpret_cast<E*>(ochunk + (uint32_t)r * rsb + ocol) = from_f32<E>(y[e]);
             }
         }
         __syncthreads();
