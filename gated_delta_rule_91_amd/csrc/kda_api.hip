@@ -6,7 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/kda.h"
+#include "kda.h"
 #include "kda_internal.hpp"
 
 using namespace kda;

@@ -11,9 +11,9 @@
 //   S <- diag(e^gamma_C) S + Ke^T U
 //
 // The columns of S never interact, so the chain of one (batch row, head) is
-// split into d_v/16 independent 16-column chains, one workgroup each; the
-// state slice (d_k x 16, fp32) lives in accumulator registers for the whole
-// sequence.  Four waves share a chain: wave w owns U/O rows 16w..16w+15 and
+// split into independent 16-column slices; a workgroup runs one or two of
+// them, and its state slices (d_k x 16 fp32 each) live in accumulator
+// registers for the whole sequence.  Four waves share a chain: wave w owns U/O rows 16w..16w+15 and
 // state rows w*d_k/4 .. (w+1)*d_k/4 - 1.  U and the operand copy of S cross
 // waves through LDS (two barriers per chunk); the card operands and the gate
 // values are prefetched from global memory four chunks ahead, straight into
@@ -47,7 +47,7 @@ template <> struct Raw4<__bf16> { typedef bf16x4 type; };
 __device__ __forceinline__ f32x4 widen4(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
 __device__ __forceinline__ f32x4 widen4(f32x4 x) { return x; }
 
-template <typename E, int DK>
+template <typename E, int DK, int NTW>
 struct ChunkOps {
     using M = MM<E>;
     static constexpr int NKD = DK / M::KS;      // k-steps over d_k
@@ -57,9 +57,9 @@ struct ChunkOps {
     typename M::frag qt[NKD];                   // Qt rows 16w..16w+15
     typename M::frag ke[MTS][NKC];              // Ke^T rows of this wave's state tiles
     typename M::frag p[NKC];                    // P rows 16w..16w+15
-    typename Raw4<E>::type wv;                  // Wv tile (accumulator order), raw
     f32x4 gc[MTS];                              // e^gamma_C for the lane's state rows
-    uint32_t graw[4];                           // output-gate pre-activations, rows 4g..4g+3 (raw bits)
+    typename Raw4<E>::type wv[NTW];             // Wv tiles (accumulator order), raw
+    uint32_t graw[NTW][4];                      // gate pre-activations, rows 4g..4g+3 (raw bits)
 };
 
 // Gate values are fetched as aligned 32-bit words (for bf16: the pair of
@@ -74,15 +74,15 @@ template <> __device__ __forceinline__ float gate_value<float>(uint32_t x, int) 
 // Byte offsets of this lane's operand fragments inside a card: the same for
 // every chunk, so each load is (uniform card base) + (32-bit lane offset) +
 // (immediate), which the compiler issues in the scalar-base form.
-template <typename E, int DK>
+template <typename E, int DK, int NTW>
 struct LaneOff {
     static constexpr int MTS = DK / 64;
-    uint32_t wk, qt, p, wv;
-    uint32_t ke[MTS], gc[MTS];
-    uint32_t gcol;   // byte offset of the (aligned) gate word for this lane's column
+    uint32_t wk, qt, p;
+    uint32_t ke[MTS], gc[MTS], wv[NTW];
+    uint32_t gcol;   // byte offset of the (aligned) gate word of this lane's column in tile 0
     int grow;        // this lane's first gate/output row inside the chunk (16w + 4g)
 
-    __device__ LaneOff(int w, int g, int n, int lane, int tile, bool vcols) {
+    __device__ LaneOff(int w, int g, int n, int lane, int tile0, bool vcols) {
         using M = MM<E>;
         using CL = Card<E, DK>;
         constexpr int FB = M::KF * (int)sizeof(E);          // bytes of one lane fragment
@@ -92,7 +92,9 @@ struct LaneOff {
         wk = (uint32_t)(CL::WK + (w * NKD * 64 + lane) * FB);
         qt = (uint32_t)(CL::QT + (w * NKD * 64 + lane) * FB);
         p = (uint32_t)(CL::P + (w * NKC * 64 + lane) * FB);
-        wv = (uint32_t)(CL::WV + (((vcols ? tile : 0) * 4 + w) * 64 + lane) * 4 * SZ);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)   // transition columns read tile 0 and discard it
+            wv[j] = (uint32_t)(CL::WV + (((vcols ? tile0 + j : 0) * 4 + w) * 64 + lane) * 4 * SZ);
 #pragma unroll
         for (int mt = 0; mt < MTS; ++mt) {
             ke[mt] = (uint32_t)(CL::KET + ((((DK / 64) * w + mt) * NKC) * 64 + lane) * FB);
@@ -111,11 +113,11 @@ __device__ __forceinline__ T ldc(const char* base, uint32_t off) {
 // card: this chunk's card (uniform); gbase: the chunk's first token row of g
 // at column col0 (uniform); rsb: bytes between tokens; nvalid: tokens of
 // this chunk inside the sequence (rows past it re-read the last one)
-template <typename E, int DK, bool SUMMARY>
-__device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, const LaneOff<E, DK>& lo,
+template <typename E, int DK, int NTW, bool SUMMARY>
+__device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* card, const LaneOff<E, DK, NTW>& lo,
                                          const char* gbase, uint32_t rsb, int nvalid) {
     using M = MM<E>;
-    using O = ChunkOps<E, DK>;
+    using O = ChunkOps<E, DK, NTW>;
     typedef typename M::frag F;
     constexpr int KSB = 64 * M::KF * (int)sizeof(E);   // bytes per fragment block (one k-step)
 #pragma unroll
@@ -126,7 +128,8 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, c
         for (int s = 0; s < O::NKC; ++s) o.ke[mt][s] = ldc<F>(card, lo.ke[mt] + s * KSB);
 #pragma unroll
     for (int mt = 0; mt < O::MTS; ++mt) o.gc[mt] = ldc<f32x4>(card, lo.gc[mt]);
-    o.wv = ldc<typename Raw4<E>::type>(card, lo.wv);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) o.wv[j] = ldc<typename Raw4<E>::type>(card, lo.wv[j]);
     if (!SUMMARY) {
 #pragma unroll
         for (int s = 0; s < O::NKD; ++s) o.qt[s] = ldc<F>(card, lo.qt + s * KSB);
@@ -135,26 +138,32 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK>& o, const char* card, c
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = lo.grow + e < nvalid ? lo.grow + e : nvalid - 1;
-            o.graw[e] = ldc<uint32_t>(gbase, (uint32_t)r * rsb + lo.gcol);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+                o.graw[j][e] = ldc<uint32_t>(gbase, (uint32_t)r * rsb + lo.gcol + 16 * j * (int)sizeof(E));
         }
     }
 }
 
-template <typename E, int DK, bool SUMMARY>
+// One workgroup = NTW adjacent 16-column slices of one (batch row, head):
+// the card fragments a wave loads serve all NTW slices.
+template <typename E, int DK, int NTW, bool SUMMARY>
 __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     using M = MM<E>;
     using CL = Card<E, DK>;
-    using O = ChunkOps<E, DK>;
+    using O = ChunkOps<E, DK, NTW>;
     constexpr int C = kChunk, KS = M::KS;
     constexpr int NT = DK / 16;                         // value-column tiles
     constexpr int NTALL = SUMMARY ? 2 * NT : NT;        // + transition-column tiles
+    constexpr int NWG = NTALL / NTW;                    // workgroups per (batch row, head)
     constexpr int PADE = 16 / (int)sizeof(E);
-    constexpr int LDS_S = DK + PADE;                    // sS[16][LDS_S]: S^T operand copy
-    constexpr int LDS_U = C + PADE;                     // sU[16][LDS_U]: U^T
+    constexpr int LDS_S = DK + PADE;                    // sS[16*NTW][LDS_S]: S^T operand copy
+    constexpr int LDS_U = C + PADE;                     // sU[16*NTW][LDS_U]: U^T
     constexpr int MTS = O::MTS;
+    static_assert(NT % NTW == 0, "slices of one workgroup never straddle value/transition columns");
 
-    __shared__ __attribute__((aligned(16))) E sS[16 * LDS_S];
-    __shared__ __attribute__((aligned(16))) E sU[16 * LDS_U];
+    __shared__ __attribute__((aligned(16))) E sS[16 * NTW * LDS_S];
+    __shared__ __attribute__((aligned(16))) E sU[16 * NTW * LDS_U];
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4, n = lane & 15;
 
@@ -164,34 +173,39 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     const int64_t x = blockIdx.x;
     const int xcd = (int)(x % kXcds);
     const int64_t slot = x / kXcds;
-    const int tile = (int)(slot % NTALL);
-    const int64_t bh = (slot / NTALL) * kXcds + xcd;
+    const int tile0 = (int)(slot % NWG) * NTW;
+    const int64_t bh = (slot / NWG) * kXcds + xcd;
     if (bh >= BH) return;
     const int64_t b = bh / H;
     const int h = (int)(bh % H);
-    const bool vcols = tile < NT;                       // value columns (else transition columns)
-    const int col0 = (vcols ? tile : tile - NT) * 16;   // first column of this slice
+    const bool vcols = tile0 < NT;                        // value columns (else transition columns)
+    const int col0 = (vcols ? tile0 : tile0 - NT) * 16;   // first column of this workgroup
 
-    // ---- initial state slice: rows (DK/4)*w + 16*mt + 4g + e, column col0 + n ----
-    f32x4 S[MTS];
+    // ---- initial state: slice j, rows (DK/4)*w + 16*mt + 4g + e, column col0 + 16j + n ----
+    f32x4 S[NTW][MTS];
 #pragma unroll
-    for (int mt = 0; mt < MTS; ++mt)
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = (DK / 4) * w + 16 * mt + 4 * g + e;
-            float s0 = 0.f;
-            if (SUMMARY) {
-                if (!vcols) s0 = (r == col0 + n) ? 1.f : 0.f;
-            } else if (a.state_in) {
-                s0 = a.state_in[((size_t)bh * DK + r) * DK + col0 + n];
+        for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = (DK / 4) * w + 16 * mt + 4 * g + e;
+                const int col = col0 + 16 * j + n;
+                float s0 = 0.f;
+                if (SUMMARY) {
+                    if (!vcols) s0 = (r == col) ? 1.f : 0.f;
+                } else if (a.state_in) {
+                    s0 = a.state_in[((size_t)bh * DK + r) * DK + col];
+                }
+                S[j][mt][e] = s0;
             }
-            S[mt][e] = s0;
-        }
 #pragma unroll
-    for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, S[mt]);
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MTS; ++mt) st4(sS + (16 * j + n) * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, S[j][mt]);
 
     const char* cards = a.ws + (size_t)bh * NC * CL::BYTES;
-    const LaneOff<E, DK> lo(w, g, n, lane, tile, vcols);
+    const LaneOff<E, DK, NTW> lo(w, g, n, lane, tile0, vcols);
     const uint32_t rsb = (uint32_t)(H * DK * (int)sizeof(E));              // bytes between tokens
     // first token row of this (b, h) at column col0, as bytes, for g and out
     const size_t head0 = (((size_t)b * a.T * H + h) * DK + col0) * sizeof(E);
@@ -205,58 +219,73 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
         const int cc = c < NC ? c : NC - 1;
         const int64_t t0 = (int64_t)cc * C;
         const int nvalid = (int)(a.T - t0 < C ? a.T - t0 : C);
-        load_ops<E, DK, SUMMARY>(o, cards + (size_t)cc * CL::BYTES, lo, gseq + (size_t)t0 * rsb, rsb, nvalid);
+        load_ops<E, DK, NTW, SUMMARY>(o, cards + (size_t)cc * CL::BYTES, lo, gseq + (size_t)t0 * rsb, rsb, nvalid);
     };
 
     auto step = [&](const O& cur, int c) {
         // S operand (B fragments) from the shared copy
-        typename M::frag sb[O::NKD];
+        typename M::frag sb[NTW][O::NKD];
 #pragma unroll
-        for (int s = 0; s < O::NKD; ++s) sb[s] = ld_frag(sS, LDS_S, n, s * KS, g);
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int s = 0; s < O::NKD; ++s) sb[j][s] = ld_frag(sS + 16 * j * LDS_S, LDS_S, n, s * KS, g);
 
         // U rows 16w..16w+15 = Wv - Wk S = -((-Wv) + Wk S)
-        f32x4 u = vcols ? -widen4(cur.wv) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < O::NKD; ++s) u = M::mma(cur.wk[s], sb[s], u);
-        u = -u;
-        st4(sU + n * LDS_U + 16 * w + 4 * g, u);
+        for (int j = 0; j < NTW; ++j) {
+            f32x4 u = vcols ? -widen4(cur.wv[j]) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < O::NKD; ++s) u = M::mma(cur.wk[s], sb[j][s], u);
+            st4(sU + (16 * j + n) * LDS_U + 16 * w + 4 * g, -u);
+        }
         __syncthreads();
 
-        typename M::frag ub[O::NKC];
+        typename M::frag ub[NTW][O::NKC];
 #pragma unroll
-        for (int s = 0; s < O::NKC; ++s) ub[s] = ld_frag(sU, LDS_U, n, s * KS, g);
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int s = 0; s < O::NKC; ++s) ub[j][s] = ld_frag(sU + 16 * j * LDS_U, LDS_U, n, s * KS, g);
 
         // S <- diag(e^gamma_C) S + Ke^T U
 #pragma unroll
-        for (int mt = 0; mt < MTS; ++mt) {
-            f32x4 acc = S[mt] * cur.gc[mt];
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-            for (int s = 0; s < O::NKC; ++s) acc = M::mma(cur.ke[mt][s], ub[s], acc);
-            S[mt] = acc;
-        }
+            for (int mt = 0; mt < MTS; ++mt) {
+                f32x4 acc = S[j][mt] * cur.gc[mt];
 #pragma unroll
-        for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, S[mt]);
+                for (int s = 0; s < O::NKC; ++s) acc = M::mma(cur.ke[mt][s], ub[j][s], acc);
+                S[j][mt] = acc;
+            }
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int mt = 0; mt < MTS; ++mt) st4(sS + (16 * j + n) * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, S[j][mt]);
 
         if (!SUMMARY) {
-            // O rows 16w..16w+15 = Qt S_old + P U (P is zero above the diagonal)
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < O::NKD; ++s) o = M::mma(cur.qt[s], sb[s], o);
-            // P is zero above the diagonal, so the full k range is exact
-#pragma unroll
-            for (int s = 0; s < O::NKC; ++s) o = M::mma(cur.p[s], ub[s], o);
-            float y[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = o[e] * sigmoidf_(gate_value<E>(cur.graw[e], n));
-            // keep the gate math out of the store branch below: inside a branch
-            // the compiler would wait for every outstanding load first
-            asm volatile("" ::"v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
             char* ochunk = oseq + (size_t)c * C * rsb;
             const int nvalid = (int)(a.T - (int64_t)c * C < C ? a.T - (int64_t)c * C : C);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = lo.grow + e;
-                if (r < nvalid) *reinterpret_cast<E*>(ochunk + (uint32_t)r * rsb + ocol) = from_f32<E>(y[e]);
+            for (int j = 0; j < NTW; ++j) {
+                // O rows 16w..16w+15 = Qt S_old + P U (P is zero above the
+                // diagonal, so the full k range is exact)
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < O::NKD; ++s) o = M::mma(cur.qt[s], sb[j][s], o);
+#pragma unroll
+                for (int s = 0; s < O::NKC; ++s) o = M::mma(cur.p[s], ub[j][s], o);
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = o[e] * sigmoidf_(gate_value<E>(cur.graw[j][e], n));
+                // keep the gate math out of the store branch below: inside a
+                // branch the compiler would wait for every outstanding load
+                asm volatile("" ::"v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = lo.grow + e;
+                    if (r < nvalid)
+                        *reinterpret_cast<E*>(ochunk + (uint32_t)r * rsb + ocol + 16 * j * (int)sizeof(E)) =
+                            from_f32<E>(y[e]);
+                }
             }
         }
         __syncthreads();
@@ -288,19 +317,41 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
         if (c + 2 < NC) step(o2, c + 2);
     }
 
-    // ---- final state slice ----
+    // ---- final state ----
 #pragma unroll
-    for (int mt = 0; mt < MTS; ++mt)
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = (DK / 4) * w + 16 * mt + 4 * g + e;
-            if (SUMMARY) {
-                if (vcols) a.zero_state[((size_t)bh * DK + r) * DK + col0 + n] = S[mt][e];
-                else a.transition[((size_t)bh * DK + r) * DK + col0 + n] = S[mt][e];
-            } else if (a.state_out) {
-                a.state_out[((size_t)bh * DK + r) * DK + col0 + n] = S[mt][e];
+        for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = (DK / 4) * w + 16 * mt + 4 * g + e;
+                const size_t idx = ((size_t)bh * DK + r) * DK + col0 + 16 * j + n;
+                if (SUMMARY) {
+                    if (vcols) a.zero_state[idx] = S[j][mt][e];
+                    else a.transition[idx] = S[j][mt][e];
+                } else if (a.state_out) {
+                    a.state_out[idx] = S[j][mt][e];
+                }
             }
-        }
+}
+
+// Slices per workgroup: two slices share each card fragment (1.5x more work
+// per compute-unit cycle, measured on the 64K-token workload) but halve the
+// workgroup count, so they are used only when that still leaves at least
+// one workgroup per compute unit.  Four slices exceed the register file.
+constexpr int kCUs = 256;
+inline int pick_ntw(int64_t BH, int NTALL) {
+    return (NTALL % 2 == 0 && BH * (NTALL / 2) >= kCUs) ? 2 : 1;
+}
+
+template <typename E, int DK, int NTW, bool SUMMARY>
+hipError_t launch_scan_n(const ScanArgs& a, hipStream_t s) {
+    constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
+    const int64_t BH = a.B * (int64_t)a.H;
+    const int64_t groups = (BH + kXcds - 1) / kXcds;
+    const int64_t blocks = groups * kXcds * (NTALL / NTW);
+    hipLaunchKernelGGL((kda_scan_kernel<E, DK, NTW, SUMMARY>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 template <typename E, int DK, bool SUMMARY>
@@ -308,10 +359,7 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
     if (BH == 0) return hipSuccess;
-    const int64_t groups = (BH + kXcds - 1) / kXcds;
-    const int64_t blocks = groups * kXcds * NTALL;
-    hipLaunchKernelGGL((kda_scan_kernel<E, DK, SUMMARY>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    return pick_ntw(BH, NTALL) == 2 ? launch_scan_n<E, DK, 2, SUMMARY>(a, s) : launch_scan_n<E, DK, 1, SUMMARY>(a, s);
 }
 
 }  // namespace
