@@ -59,17 +59,8 @@ struct ChunkOps {
     typename M::frag p[NKC];                    // P rows 16w..16w+15
     f32x4 gc[MTS];                              // e^gamma_C for the lane's state rows
     typename Raw4<E>::type wv[NTW];             // Wv tiles (accumulator order), raw
-    uint32_t graw[NTW][4];                      // gate pre-activations, rows 4g..4g+3 (raw bits)
+    typename Raw4<E>::type graw[NTW];           // gate pre-activations: token n, columns 4g..4g+3 (raw)
 };
-
-// Gate values are fetched as aligned 32-bit words (for bf16: the pair of
-// columns holding this lane's column) -- plain dword loads keep the load
-// counter bookkeeping exact -- and decoded at the point of use.
-template <typename E> __device__ __forceinline__ float gate_value(uint32_t x, int n);
-template <> __device__ __forceinline__ float gate_value<__bf16>(uint32_t x, int n) {
-    return __uint_as_float((n & 1) ? (x & 0xffff0000u) : (x << 16));
-}
-template <> __device__ __forceinline__ float gate_value<float>(uint32_t x, int) { return __uint_as_float(x); }
 
 // Byte offsets of this lane's operand fragments inside a card: the same for
 // every chunk, so each load is (uniform card base) + (32-bit lane offset) +
@@ -79,8 +70,8 @@ struct LaneOff {
     static constexpr int MTS = DK / 64;
     uint32_t wk, qt, p;
     uint32_t ke[MTS], gc[MTS], wv[NTW];
-    uint32_t gcol;   // byte offset of the (aligned) gate word of this lane's column in tile 0
-    int grow;        // this lane's first gate/output row inside the chunk (16w + 4g)
+    uint32_t gcol;   // byte offset of this lane's 4 gate/output columns (4g..4g+3) in slice 0
+    int grow;        // this lane's gate/output row inside the chunk (16w + n)
 
     __device__ LaneOff(int w, int g, int n, int lane, int tile0, bool vcols) {
         using M = MM<E>;
@@ -100,8 +91,8 @@ struct LaneOff {
             ke[mt] = (uint32_t)(CL::KET + ((((DK / 64) * w + mt) * NKC) * 64 + lane) * FB);
             gc[mt] = (uint32_t)(CL::GC + ((DK / 4) * w + 16 * mt + 4 * g) * 4);
         }
-        gcol = (uint32_t)((SZ == 2 ? (n & ~1) : n) * SZ);
-        grow = 16 * w + 4 * g;
+        gcol = (uint32_t)(4 * g * SZ);
+        grow = 16 * w + n;
     }
 };
 
@@ -135,13 +126,10 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
         for (int s = 0; s < O::NKD; ++s) o.qt[s] = ldc<F>(card, lo.qt + s * KSB);
 #pragma unroll
         for (int s = 0; s < O::NKC; ++s) o.p[s] = ldc<F>(card, lo.p + s * KSB);
+        const int r = lo.grow < nvalid ? lo.grow : nvalid - 1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = lo.grow + e < nvalid ? lo.grow + e : nvalid - 1;
-#pragma unroll
-            for (int j = 0; j < NTW; ++j)
-                o.graw[j][e] = ldc<uint32_t>(gbase, (uint32_t)r * rsb + lo.gcol + 16 * j * (int)sizeof(E));
-        }
+        for (int j = 0; j < NTW; ++j)
+            o.graw[j] = ldc<typename Raw4<E>::type>(gbase, (uint32_t)r * rsb + lo.gcol + 16 * j * (int)sizeof(E));
     }
 }
 
@@ -211,7 +199,6 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     const size_t head0 = (((size_t)b * a.T * H + h) * DK + col0) * sizeof(E);
     const char* gseq = reinterpret_cast<const char*>(a.g) + head0;
     char* oseq = reinterpret_cast<char*>(a.out) + head0;
-    const uint32_t ocol = (uint32_t)(n * (int)sizeof(E));
 
     // prefetches past the last chunk re-read the last card (never used), so
     // the steady-state loop has no branches around its loads
@@ -266,26 +253,27 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
             const int nvalid = (int)(a.T - (int64_t)c * C < C ? a.T - (int64_t)c * C : C);
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
-                // O rows 16w..16w+15 = Qt S_old + P U (P is zero above the
-                // diagonal, so the full k range is exact)
+                // O^T (16 columns x this wave's 16 tokens) = S_old^T Qt^T + U^T P^T.
+                // A 16x16 A fragment and B fragment share one lane layout, so
+                // the S/U B fragments serve as the A operands and the Qt/P A
+                // fragments as the B operands.  Lane (g, n) then holds token
+                // 16w + n, columns 4g..4g+3: one 4-element gate load and one
+                // 4-element output store.  (P is zero above the diagonal, so
+                // the full k range is exact.)
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < O::NKD; ++s) o = M::mma(cur.qt[s], sb[j][s], o);
+                for (int s = 0; s < O::NKD; ++s) o = M::mma(sb[j][s], cur.qt[s], o);
 #pragma unroll
-                for (int s = 0; s < O::NKC; ++s) o = M::mma(cur.p[s], ub[j][s], o);
-                float y[4];
+                for (int s = 0; s < O::NKC; ++s) o = M::mma(ub[j][s], cur.p[s], o);
+                const f32x4 gg = widen4(cur.graw[j]);
+                f32x4 y;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = o[e] * sigmoidf_(gate_value<E>(cur.graw[j][e], n));
+                for (int e = 0; e < 4; ++e) y[e] = o[e] * sigmoidf_(gg[e]);
                 // keep the gate math out of the store branch below: inside a
                 // branch the compiler would wait for every outstanding load
                 asm volatile("" ::"v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = lo.grow + e;
-                    if (r < nvalid)
-                        *reinterpret_cast<E*>(ochunk + (uint32_t)r * rsb + ocol + 16 * j * (int)sizeof(E)) =
-                            from_f32<E>(y[e]);
-                }
+                if (lo.grow < nvalid)
+                    st4(reinterpret_cast<E*>(ochunk + (uint32_t)lo.grow * rsb + lo.gcol + 16 * j * (int)sizeof(E)), y);
             }
         }
         __syncthreads();
