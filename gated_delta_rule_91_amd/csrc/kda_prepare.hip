@@ -12,7 +12,7 @@
 //   Qt = q^ e^gamma,  Kt = k^ e^gamma,  Kh = k^ e^-gamma,  Ke = k^ e^(gamma_C - gamma)
 //   L  = strict_lower(Kt Kh^T) (the intra-chunk correction matrix),
 //   P  = lower_incl(Qt Kh^T)
-//   T  = (I + diag(beta) L)^-1,  Wk = T diag(beta) Kt,  Wv = T diag(beta) V
+//   T  = (I + diag(beta) L)^-1,  M = T diag(beta),  Wk = M Kt,  Wv = M V
 //
 // One workgroup (4 waves) per chunk-head.  Phases:
 //   A  coalesced loads (one wave-instruction = one token row), floored
@@ -20,9 +20,9 @@
 //      cross-group offset through LDS), q/k norms (wave reductions), decay
 //      folding; Kt/Kh/Qt to LDS, Ke^T and e^gamma_C straight to the card
 //   B  L and P on MFMA (10 lower tiles each)
-//   C  Qt and P to the card; diag(beta) L to LDS in fp32
+//   C  Qt and P (staged in LDS) to the card; diag(beta) L to LDS in fp32
 //   D  T by blocked substitution in fp32: 16x16 diagonal blocks by forward
-//      substitution, off-diagonal blocks with fp32 MFMA
+//      substitution, off-diagonal blocks with fp32 MFMA; M = T diag(beta)
 //   E  Wk and Wv on MFMA (block-lower-triangular T); Wv to the card in
 //      accumulator order, Wk through LDS to the card in fragment order
 // Qt, Ke^T, P and Wk leave in MFMA A-fragment order (Card, kda_common.hpp).
@@ -111,15 +111,17 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     constexpr int TPG = C / NG;         // tokens per group
     constexpr int LDR = LY::LDR, LDT = LY::LDT, LDA = LY::LDA;
     constexpr int NT = DK / 16;         // 16-wide column tiles
+    constexpr float kLog2e = 1.4426950408889634f;
 
     __shared__ __attribute__((aligned(16))) char lds[LY::BYTES];
     E* sKt = reinterpret_cast<E*>(lds + LY::R0);     // phase A-B: Kt row-major
     E* sKh = reinterpret_cast<E*>(lds + LY::R1);     // phase A-B: Kh row-major
     E* sQt = reinterpret_cast<E*>(lds + LY::R2);     // phase A-C: Qt row-major
-    E* sKbT = reinterpret_cast<E*>(lds + LY::R0);    // phase C-E: (beta Kt)^T
-    E* sVbT = reinterpret_cast<E*>(lds + LY::R1);    // phase C-E: (beta V)^T
+    E* sKtT = reinterpret_cast<E*>(lds + LY::R0);    // phase C-E: Kt^T
+    E* sVT = reinterpret_cast<E*>(lds + LY::R1);     // phase C-E: V^T
     float* sA = reinterpret_cast<float*>(lds + LY::R2);   // phase C-D: diag(beta) L -> T (fp32)
-    E* sTb = reinterpret_cast<E*>(lds + LY::R4);     // phase D-E: T as MFMA operand
+    E* sP = reinterpret_cast<E*>(lds + LY::R4);      // phase C: P staging (row-major, ld LDT)
+    E* sTb = reinterpret_cast<E*>(lds + LY::R4);     // phase D-E: T diag(beta) as MFMA operand
     E* sWk = reinterpret_cast<E*>(lds + LY::R0);     // phase E: Wk staging
     float* sTot = reinterpret_cast<float*>(lds + LY::TOT);
     float* sBeta = reinterpret_cast<float*>(lds + LY::BETA);
@@ -127,10 +129,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     float* sRk = reinterpret_cast<float*>(lds + LY::RK);
 
     const int t = threadIdx.x;
-    const int lane = t & 63, w = t >> 6, g = lane >> 4, n = lane & 15;
+    const int lane = t & 63, g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index (uniform)
 
     // block -> (b, chunk, h): heads fastest, so neighbouring workgroups read
-    // neighbouring 256-byte pieces of the same token rows
+    // neighbouring pieces of the same token rows
     const int H = a.H, NC = a.NC;
     const int64_t T = a.T;
     const int64_t wg = blockIdx.x;
@@ -140,53 +143,44 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     const int64_t b = rest / NC;
     const int64_t tok0 = (int64_t)c * C;
     char* card = a.ws + (((size_t)b * H + h) * NC + c) * CL::BYTES;
-    const E* q = reinterpret_cast<const E*>(a.q);
-    const E* k = reinterpret_cast<const E*>(a.k);
-    const E* v = reinterpret_cast<const E*>(a.v);
-    (void)tok0;
 
     // ---------------- phase A ----------------
     // Log-decay is carried in base-2 units (lambda * log2 e) so every
     // exponential is a single v_exp_f32; e^-gamma comes from v_rcp_f32.
-    constexpr float kLog2e = 1.4426950408889634f;
-    const int cp = t % CP, grp = t / CP, c0 = 2 * cp;
-    // per-workgroup base pointers; per-token offsets stay 32-bit (a chunk of
-    // one head spans at most 64 * H * DK elements)
+    const int cp = t % CP, c0 = 2 * cp;
+    const int grp = (CP == 64) ? w : t / CP;   // at d_k = 128 a token group is a wave
     const size_t row0 = ((size_t)b * T + tok0) * H + h;
+    const size_t tstride = (size_t)H * DK;
     const float* la_b = a.log_alpha + row0 * DK;
-    const E* q_b = q + row0 * DK;
-    const E* k_b = k + row0 * DK;
-    const E* v_b = v + row0 * DK;
-    const uint32_t tstride = (uint32_t)H * DK;
+    const E* q_b = reinterpret_cast<const E*>(a.q) + row0 * DK;
+    const E* k_b = reinterpret_cast<const E*>(a.k) + row0 * DK;
+    const E* v_b = reinterpret_cast<const E*>(a.v) + row0 * DK;
     const int nvalid = (int)((T - tok0) < C ? (T - tok0) : C);
-    // Loads are unconditional (a padded token re-reads the last valid row and
-    // is zeroed afterwards): a load under a branch would be followed by a
-    // full wait on every outstanding load, serialising the chunk's fetches.
+    // Loads are unconditional: a padded token re-reads the last valid row (a
+    // load under a branch would be followed by a wait on every outstanding
+    // load).  Padding is an exact identity step as long as its beta and
+    // lambda are zero: then its rows of Wk, Wv and U vanish and its q, k, v
+    // never reach an output.
+    // per-token row pointers are uniform within a wave at d_k = 128 (scalar
+    // registers); the lane's channel pair is a 32-bit byte offset
+    const uint32_t lo_a = (uint32_t)c0 * 4u, lo_e = (uint32_t)c0 * (uint32_t)sizeof(E);
     float lam[TPG][2], qv[TPG][2], kv[TPG][2], vv[TPG][2];
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
         const int tl = grp * TPG + i;
-        const uint32_t off = (uint32_t)(tl < nvalid ? tl : nvalid - 1) * tstride + c0;
-        const f32x2 l2 = *reinterpret_cast<const f32x2*>(la_b + off);
-        const f32x2 q2 = ld2(q_b + off), k2 = ld2(k_b + off), v2 = ld2(v_b + off);
-        lam[i][0] = l2[0]; lam[i][1] = l2[1];
+        const size_t toff = (size_t)(tl < nvalid ? tl : nvalid - 1) * tstride;
+        const f32x2 l2 = *reinterpret_cast<const f32x2*>(reinterpret_cast<const char*>(la_b + toff) + lo_a);
+        const f32x2 q2 = ld2(reinterpret_cast<const E*>(reinterpret_cast<const char*>(q_b + toff) + lo_e));
+        const f32x2 k2 = ld2(reinterpret_cast<const E*>(reinterpret_cast<const char*>(k_b + toff) + lo_e));
+        const f32x2 v2 = ld2(reinterpret_cast<const E*>(reinterpret_cast<const char*>(v_b + toff) + lo_e));
+        const bool ok = tl < nvalid;
+        lam[i][0] = ok ? fmaxf(l2[0], a.floor_) * kLog2e : 0.f;
+        lam[i][1] = ok ? fmaxf(l2[1], a.floor_) * kLog2e : 0.f;
         qv[i][0] = q2[0]; qv[i][1] = q2[1];
         kv[i][0] = k2[0]; kv[i][1] = k2[1];
         vv[i][0] = v2[0]; vv[i][1] = v2[1];
     }
-    float btok = 0.f;
-    if (t < C) btok = a.beta[row0 + (size_t)(t < nvalid ? t : nvalid - 1) * H];
-#pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-        // identity padding: lambda = 0, q = k = v = 0 (and beta = 0 below)
-        const bool ok = grp * TPG + i < nvalid;
-        lam[i][0] = ok ? fmaxf(lam[i][0], a.floor_) * kLog2e : 0.f;
-        lam[i][1] = ok ? fmaxf(lam[i][1], a.floor_) * kLog2e : 0.f;
-        qv[i][0] = ok ? qv[i][0] : 0.f; qv[i][1] = ok ? qv[i][1] : 0.f;
-        kv[i][0] = ok ? kv[i][0] : 0.f; kv[i][1] = ok ? kv[i][1] : 0.f;
-        vv[i][0] = ok ? vv[i][0] : 0.f; vv[i][1] = ok ? vv[i][1] : 0.f;
-    }
-    if (t < C) sBeta[t] = (t < nvalid) ? btok : 0.f;
+    if (t < C) sBeta[t] = (t < nvalid) ? a.beta[row0 + (size_t)(t < nvalid ? t : nvalid - 1) * H] : 0.f;
     // inclusive cumulative log-decay inside the group
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
@@ -228,25 +222,25 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
         if (gg < grp) { off0 += x0; off1 += x1; }
         tot0 += x0; tot1 += x1;
     }
-    float kb[TPG][2], vb[TPG][2], ke[TPG][2];
+    // e^gamma_C per key channel: Ke = k^ e^(gamma_C - gamma) = Kh * e^gamma_C
+    const float gc0 = __builtin_amdgcn_exp2f(tot0), gc1 = __builtin_amdgcn_exp2f(tot1);
+    float kt[TPG][2], ke[TPG][2];
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
         const int tl = grp * TPG + i;
-        const float bt = sBeta[tl], rq = sRq[tl], rk = sRk[tl];
-        const float g0 = lam[i][0] + off0, g1 = lam[i][1] + off1;
-        const float e0 = __builtin_amdgcn_exp2f(g0), e1 = __builtin_amdgcn_exp2f(g1);
+        const float rq = sRq[tl], rk = sRk[tl];
+        const float e0 = __builtin_amdgcn_exp2f(lam[i][0] + off0), e1 = __builtin_amdgcn_exp2f(lam[i][1] + off1);
         const float ei0 = __builtin_amdgcn_rcpf(e0), ei1 = __builtin_amdgcn_rcpf(e1);
         const float kn0 = kv[i][0] * rk, kn1 = kv[i][1] * rk;
         const float qn0 = qv[i][0] * rq, qn1 = qv[i][1] * rq;
-        st2(sKt + tl * LDR + c0, kn0 * e0, kn1 * e1);
-        st2(sKh + tl * LDR + c0, kn0 * ei0, kn1 * ei1);
+        kt[i][0] = kn0 * e0;
+        kt[i][1] = kn1 * e1;
+        const float kh0 = kn0 * ei0, kh1 = kn1 * ei1;
+        st2(sKt + tl * LDR + c0, kt[i][0], kt[i][1]);
+        st2(sKh + tl * LDR + c0, kh0, kh1);
         st2(sQt + tl * LDR + c0, qn0 * e0, qn1 * e1);
-        ke[i][0] = kn0 * __builtin_amdgcn_exp2f(tot0 - g0);
-        ke[i][1] = kn1 * __builtin_amdgcn_exp2f(tot1 - g1);
-        kb[i][0] = bt * (kn0 * e0);
-        kb[i][1] = bt * (kn1 * e1);
-        vb[i][0] = bt * vv[i][0];
-        vb[i][1] = bt * vv[i][1];
+        ke[i][0] = kh0 * gc0;
+        ke[i][1] = kh1 * gc1;
     }
     {   // Ke^T rows c0, c0+1 (key channels), columns = this group's TPG tokens,
         // written in fragment order
@@ -266,14 +260,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
                 for (int j = 0; j < TPG; ++j) keT[frag_index<E>(c0 + ch, grp * TPG + j, C)] = from_f32<E>(ke[j][ch]);
             }
         }
-        if (grp == 0) {
-            float* gc = reinterpret_cast<float*>(card + CL::GC);
-            *reinterpret_cast<f32x2*>(gc + c0) = f32x2{__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1)};
-        }
+        if (grp == 0) *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(card + CL::GC) + c0) = f32x2{gc0, gc1};
     }
     __syncthreads();
 
     // ---------------- phase B: L = Kt Kh^T, P = Qt Kh^T (lower tiles) ----------------
+    // diag(beta) L needs no mask: the inversion reads only strictly-lower
+    // entries of the diagonal tiles.  P is masked on its diagonal tiles.
     f32x4 acc[5];
 #pragma unroll
     for (int r = 0; r < 5; ++r) {
@@ -287,12 +280,14 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
 #pragma unroll
         for (int s = 0; s < DK / KS; ++s)
             x = M::mma(ld_frag(src, LDR, 16 * ti + n, s * KS, g), ld_frag(sKh, LDR, 16 * tj + n, s * KS, g), x);
-        // masks: L strictly lower (scaled by beta of the row), P lower incl.
+        if (isP) {
+            if (ti == tj) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * ti + 4 * g + e, col = 16 * tj + n;
-            if (isP) x[e] = (col <= row) ? x[e] : 0.f;
-            else x[e] = (col < row) ? x[e] * sBeta[row] : 0.f;
+                for (int e = 0; e < 4; ++e) x[e] = (n <= 4 * g + e) ? x[e] : 0.f;
+            }
+        } else {
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(sBeta + 16 * ti + 4 * g);
+            x *= bt;
         }
         acc[r] = x;
     }
@@ -300,37 +295,34 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
 
     // ---------------- phase C ----------------
 #pragma unroll
-    for (int i = 0; i < TPG; i += 4) {   // (beta Kt)^T and (beta V)^T, TPG tokens per row
+    for (int i = 0; i < TPG; i += 4) {   // Kt^T and V^T, TPG tokens per row
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            st4(sKbT + (c0 + ch) * LDT + grp * TPG + i, f32x4{kb[i][ch], kb[i + 1][ch], kb[i + 2][ch], kb[i + 3][ch]});
-            st4(sVbT + (c0 + ch) * LDT + grp * TPG + i, f32x4{vb[i][ch], vb[i + 1][ch], vb[i + 2][ch], vb[i + 3][ch]});
+            st4(sKtT + (c0 + ch) * LDT + grp * TPG + i, f32x4{kt[i][ch], kt[i + 1][ch], kt[i + 2][ch], kt[i + 3][ch]});
+            st4(sVT + (c0 + ch) * LDT + grp * TPG + i, f32x4{vv[i][ch], vv[i + 1][ch], vv[i + 2][ch], vv[i + 3][ch]});
         }
+    }
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {   // P -> LDS staging: the 10 lower tiles ...
+        const int tau = w + 4 * r;
+        if (tau >= 10) {
+            const int id = tau - 10;
+            const int ti = (id >= 1) + (id >= 3) + (id >= 6);
+            const int tj = id - ti * (ti + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sP[(16 * ti + 4 * g + e) * LDT + 16 * tj + n] = from_f32<E>(acc[r][e]);
+        }
+    }
+    for (int idx = t; idx < 6 * 64; idx += kThreads) {   // ... and zeros for the 6 upper tiles
+        const int ut = idx >> 6, el = (idx & 63) * 4;     // 4 elements per item
+        // upper tiles (ti, tj), tj > ti: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int ti = (ut >= 3) + (ut >= 5);
+        const int tj = ut - (ti == 0 ? 0 : (ti == 1 ? 3 : 5)) + ti + 1;
+        st4(sP + (16 * ti + (el >> 4)) * LDT + 16 * tj + (el & 15), f32x4{0.f, 0.f, 0.f, 0.f});
     }
     store_frag_order<E, C, DK>(card + CL::QT, sQt, LDR, t);   // Qt -> card
-    {   // P -> card: the 10 computed lower tiles, then zeros for the 6 upper tiles
-        E* cp_ = reinterpret_cast<E*>(card + CL::P);
-#pragma unroll
-        for (int r = 0; r < 5; ++r) {
-            const int tau = w + 4 * r;
-            if (tau >= 10) {
-                const int id = tau - 10;
-                const int ti = (id >= 1) + (id >= 3) + (id >= 6);
-                const int tj = id - ti * (ti + 1) / 2;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    cp_[frag_index<E>(16 * ti + 4 * g + e, 16 * tj + n, C)] = from_f32<E>(acc[r][e]);
-            }
-        }
-        for (int idx = t; idx < 6 * 256; idx += kThreads) {
-            const int ut = idx >> 8, el = idx & 255;
-            // upper tiles (ti, tj), tj > ti: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-            const int ti = (ut >= 3) + (ut >= 5);
-            const int tj = ut - (ti == 0 ? 0 : (ti == 1 ? 3 : 5)) + ti + 1;
-            cp_[frag_index<E>(16 * ti + (el >> 4), 16 * tj + (el & 15), C)] = from_f32<E>(0.f);
-        }
-    }
     __syncthreads();
+    store_frag_order<E, C, C>(card + CL::P, sP, LDT, t);      // P -> card
 #pragma unroll
     for (int r = 0; r < 5; ++r) {   // diag(beta) L -> sA (fp32; overwrites Qt)
         const int tau = w + 4 * r;
@@ -389,17 +381,18 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
         }
         __syncthreads();
     }
-    // D3: T -> MFMA operand type, zero above the diagonal
+    // D3: M = T diag(beta) -> MFMA operand type, zero above the diagonal
     for (int idx = t; idx < C * C / 4; idx += kThreads) {
         const int row = idx / (C / 4), col = (idx % (C / 4)) * 4;
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(sBeta + col);
         f32x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (col + e <= row) ? sA[row * LDA + col + e] : 0.f;
+        for (int e = 0; e < 4; ++e) x[e] = (col + e <= row) ? sA[row * LDA + col + e] * bt[e] : 0.f;
         st4(sTb + row * LDT + col, x);
     }
     __syncthreads();
 
-    // ---------------- phase E: Wk = T (beta Kt), Wv = T (beta V) ----------------
+    // ---------------- phase E: Wk = M Kt, Wv = M V ----------------
     constexpr int NTW = NT / 4;   // column tiles per wave
     f32x4 wk[NTW][4];
 #pragma unroll
@@ -408,14 +401,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xv = {0.f, 0.f, 0.f, 0.f};
-            constexpr int dummy = 0; (void)dummy;
             const int nks = (16 * (mi + 1) + KS - 1) / KS;
 #pragma unroll
             for (int s = 0; s < (C / KS); ++s) {
                 if (s < nks) {
                     const auto af = ld_frag(sTb, LDT, 16 * mi + n, s * KS, g);
-                    xk = M::mma(af, ld_frag(sKbT, LDT, 16 * ni + n, s * KS, g), xk);
-                    xv = M::mma(af, ld_frag(sVbT, LDT, 16 * ni + n, s * KS, g), xv);
+                    xk = M::mma(af, ld_frag(sKtT, LDT, 16 * ni + n, s * KS, g), xk);
+                    xv = M::mma(af, ld_frag(sVT, LDT, 16 * ni + n, s * KS, g), xv);
                 }
             }
             st4(reinterpret_cast<E*>(card + CL::WV) + ((size_t)(ni * 4 + mi) * 64 + lane) * 4, xv);
