@@ -35,7 +35,7 @@ C = 64
 D = 128
 # algorithmic bytes per token-head (bf16 I/O, fp32 log-decay and beta):
 PATH_BYTES = 4 * D * 2 + D * 4 + 4 + D * 2          # q,k,v,g in; log_alpha, beta in; out -> 1,796
-CARD_BYTES = 74240 // C                               # update card per token-head (bf16, d=128) -> 1,160
+CARD_BYTES = 74240 // C    # update card per token-head (bf16, d=128; meaningful bytes, 1 KB padding excluded) -> 1,160
 PREP_BYTES = 3 * D * 2 + D * 4 + 4 + CARD_BYTES       # q,k,v,log_alpha,beta in; card out -> 2,444
 SCAN_BYTES = CARD_BYTES + D * 2 + D * 2               # card, g in; out -> 1,672
 # algorithmic FLOPs per token-head of the chunk method (triangular C x C products at half):

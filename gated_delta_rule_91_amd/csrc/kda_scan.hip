@@ -60,6 +60,7 @@ struct ChunkOps {
     f32x4 gc[MTS];                              // e^gamma_C for the lane's state rows
     typename Raw4<E>::type wv[NTW];             // Wv tiles (accumulator order), raw
     typename Raw4<E>::type graw[NTW];           // gate pre-activations: token n, columns 4g..4g+3 (raw)
+    uint32_t pf;                                // L2 prefetch of a later card (value unused)
 };
 
 // Byte offsets of this lane's operand fragments inside a card: the same for
@@ -135,6 +136,11 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
 
 // One workgroup = NTW adjacent 16-column slices of one (batch row, head):
 // the card fragments a wave loads serve all NTW slices.
+// Depth of the operand ring (chunks of card fragments in flight per wave),
+// and how far past the ring's newest chunk the L2 prefetch runs.
+constexpr int kRing = 4;
+constexpr int kPrefetch = kRing + 1;
+
 template <typename E, int DK, int NTW, bool SUMMARY>
 __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     using M = MM<E>;
@@ -202,14 +208,25 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
 
     // prefetches past the last chunk re-read the last card (never used), so
     // the steady-state loop has no branches around its loads
+    // The workgroups of one (row, head) read the same cards; each also pulls
+    // its share of the card kPrefetch chunks past the ring into L2 (one dword
+    // per 128-byte line), so the ring loads of all of them hit in L2 instead of
+    // all waiting on the same HBM misses.
+    constexpr int NL = (int)(CL::BYTES / 128);                 // lines per card
+    constexpr int LPW = (NL + NWG - 1) / NWG;                  // lines per workgroup
+    const int pline = (int)(slot % NWG) * LPW + (w * 64 + lane < LPW ? w * 64 + lane : LPW - 1);
+    const uint32_t poff = (uint32_t)((pline < NL ? pline : NL - 1) * 128);
     auto load = [&](O& o, int c) {
         const int cc = c < NC ? c : NC - 1;
         const int64_t t0 = (int64_t)cc * C;
         const int nvalid = (int)(a.T - t0 < C ? a.T - t0 : C);
         load_ops<E, DK, NTW, SUMMARY>(o, cards + (size_t)cc * CL::BYTES, lo, gseq + (size_t)t0 * rsb, rsb, nvalid);
+        const int cp = c + kPrefetch < NC ? c + kPrefetch : NC - 1;
+        o.pf = ldc<uint32_t>(cards + (size_t)cp * CL::BYTES, poff);
     };
 
     auto step = [&](const O& cur, int c) {
+        asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
         // S operand (B fragments) from the shared copy
         typename M::frag sb[NTW][O::NKD];
 #pragma unroll
@@ -279,30 +296,36 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
         __syncthreads();
     };
 
-    // four chunks of operands in flight: chunk c + 4 is requested as soon as
-    // chunk c's registers are free.  The loop body is branch-free so the
-    // load-counter waits stay exact; up to three chunks finish in the tail.
+    // kRing chunks of operands in flight: chunk c + kRing is requested as soon
+    // as chunk c's registers are free.  The loop body is branch-free so the
+    // load-counter waits stay exact; up to kRing - 1 chunks finish in the tail.
+    // (Named ring slots: an array of them allocates worse.)
+    static_assert(kRing >= 2 && kRing <= 4, "ring depth");
     if (NC > 0) {
         O o0, o1, o2, o3;
         load(o0, 0);
         load(o1, 1);
-        load(o2, 2);
-        load(o3, 3);
+        if (kRing > 2) load(o2, 2);
+        if (kRing > 3) load(o3, 3);
         __syncthreads();
         int c = 0;
-        for (; c + 4 <= NC; c += 4) {
+        for (; c + kRing <= NC; c += kRing) {
             step(o0, c);
-            load(o0, c + 4);
+            load(o0, c + kRing);
             step(o1, c + 1);
-            load(o1, c + 5);
-            step(o2, c + 2);
-            load(o2, c + 6);
-            step(o3, c + 3);
-            load(o3, c + 7);
+            load(o1, c + kRing + 1);
+            if (kRing > 2) {
+                step(o2, c + 2);
+                load(o2, c + kRing + 2);
+            }
+            if (kRing > 3) {
+                step(o3, c + 3);
+                load(o3, c + kRing + 3);
+            }
         }
         if (c < NC) step(o0, c);
-        if (c + 1 < NC) step(o1, c + 1);
-        if (c + 2 < NC) step(o2, c + 2);
+        if (kRing > 2 && c + 1 < NC) step(o1, c + 1);
+        if (kRing > 3 && c + 2 < NC) step(o2, c + 2);
     }
 
     // ---- final state ----
