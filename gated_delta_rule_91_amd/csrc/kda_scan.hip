@@ -31,6 +31,8 @@
 // to the 8 XCDs, so the tiles of one head are given ids that are congruent
 // mod 8 and share one XCD's L2, where the head's cards are read by all of
 // its chains.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -225,7 +227,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
         o.pf = ldc<uint32_t>(cards + (size_t)cp * CL::BYTES, poff);
     };
 
-    auto step = [&](const O& cur, int c) {
+    // FULL: the chunk holds C tokens, so its output stores are unconditional
+    // (a store under a branch leaves the compiler unsure how many accesses are
+    // in flight, and every later wait would tighten by one)
+    auto step = [&](auto full, const O& cur, int c) {
+        constexpr bool FULL = decltype(full)::value;
         asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
         // S operand (B fragments) from the shared copy
         typename M::frag sb[NTW][O::NKD];
@@ -288,8 +294,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
                 for (int e = 0; e < 4; ++e) y[e] = o[e] * sigmoidf_(gg[e]);
                 // keep the gate math out of the store branch below: inside a
                 // branch the compiler would wait for every outstanding load
-                asm volatile("" ::"v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
-                if (lo.grow < nvalid)
+                if (!FULL) asm volatile("" ::"v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
+                if (FULL || lo.grow < nvalid)
                     st4(reinterpret_cast<E*>(ochunk + (uint32_t)lo.grow * rsb + lo.gcol + 16 * j * (int)sizeof(E)), y);
             }
         }
@@ -298,10 +304,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
 
     // kRing chunks of operands in flight: chunk c + kRing is requested as soon
     // as chunk c's registers are free.  The loop body is branch-free so the
-    // load-counter waits stay exact; up to kRing - 1 chunks finish in the tail.
-    // (Named ring slots: an array of them allocates worse.)
+    // load-counter waits stay exact.  It runs over full chunks only; the
+    // rest (fewer than kRing full chunks, then a partial one) finish in the
+    // tail from the slots already loaded.  (Named ring slots: an array of
+    // them allocates worse.)
     static_assert(kRing >= 2 && kRing <= 4, "ring depth");
     if (NC > 0) {
+        using Full = std::integral_constant<bool, true>;
+        using Part = std::integral_constant<bool, false>;
+        const int NCF = (int64_t)NC * C > a.T ? NC - 1 : NC;   // full chunks
         O o0, o1, o2, o3;
         load(o0, 0);
         load(o1, 1);
@@ -309,23 +320,24 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
         if (kRing > 3) load(o3, 3);
         __syncthreads();
         int c = 0;
-        for (; c + kRing <= NC; c += kRing) {
-            step(o0, c);
+        for (; c + kRing <= NCF; c += kRing) {
+            step(Full{}, o0, c);
             load(o0, c + kRing);
-            step(o1, c + 1);
+            step(Full{}, o1, c + 1);
             load(o1, c + kRing + 1);
             if (kRing > 2) {
-                step(o2, c + 2);
+                step(Full{}, o2, c + 2);
                 load(o2, c + kRing + 2);
             }
             if (kRing > 3) {
-                step(o3, c + 3);
+                step(Full{}, o3, c + 3);
                 load(o3, c + kRing + 3);
             }
         }
-        if (c < NC) step(o0, c);
-        if (kRing > 2 && c + 1 < NC) step(o1, c + 1);
-        if (kRing > 3 && c + 2 < NC) step(o2, c + 2);
+        if (c < NC) step(Part{}, o0, c);
+        if (c + 1 < NC) step(Part{}, o1, c + 1);
+        if (kRing > 2 && c + 2 < NC) step(Part{}, o2, c + 2);
+        if (kRing > 3 && c + 3 < NC) step(Part{}, o3, c + 3);
     }
 
     // ---- final state ----
