@@ -59,7 +59,7 @@ struct ChunkOps {
     typename M::frag qt[NKD];                   // Qt rows 16w..16w+15
     typename M::frag ke[MTS][NKC];              // Ke^T rows of this wave's state tiles
     typename M::frag p[NKC];                    // P rows 16w..16w+15
-    f32x4 gc[MTS];                              // e^gamma_C for the lane's state rows
+    float gc;                                   // e^gamma_C of state row (d_k/4)w + (lane mod d_k/4)
     typename Raw4<E>::type wv[NTW];             // Wv tiles (accumulator order), raw
     typename Raw4<E>::type graw[NTW];           // gate pre-activations: token n, columns 4g..4g+3 (raw)
     uint32_t pf;                                // L2 prefetch of a later card (value unused)
@@ -72,7 +72,7 @@ template <typename E, int DK, int NTW>
 struct LaneOff {
     static constexpr int MTS = DK / 64;
     uint32_t wk, qt, p;
-    uint32_t ke[MTS], gc[MTS], wv[NTW];
+    uint32_t ke[MTS], gc, wv[NTW];
     uint32_t gcol;   // byte offset of this lane's 4 gate/output columns (4g..4g+3) in slice 0
     int grow;        // this lane's gate/output row inside the chunk (16w + n)
 
@@ -92,8 +92,9 @@ struct LaneOff {
 #pragma unroll
         for (int mt = 0; mt < MTS; ++mt) {
             ke[mt] = (uint32_t)(CL::KET + ((((DK / 64) * w + mt) * NKC) * 64 + lane) * FB);
-            gc[mt] = (uint32_t)(CL::GC + ((DK / 4) * w + 16 * mt + 4 * g) * 4);
         }
+        // one dword per lane: the wave's d_k/4 state rows (repeated across lanes)
+        gc = (uint32_t)(CL::GC + ((DK / 4) * w + lane % (DK / 4)) * 4);
         gcol = (uint32_t)(4 * g * SZ);
         grow = 16 * w + n;
     }
@@ -120,8 +121,7 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
     for (int mt = 0; mt < O::MTS; ++mt)
 #pragma unroll
         for (int s = 0; s < O::NKC; ++s) o.ke[mt][s] = ldc<F>(card, lo.ke[mt] + s * KSB);
-#pragma unroll
-    for (int mt = 0; mt < O::MTS; ++mt) o.gc[mt] = ldc<f32x4>(card, lo.gc[mt]);
+    o.gc = ldc<float>(card, lo.gc);
 #pragma unroll
     for (int j = 0; j < NTW; ++j) o.wv[j] = ldc<typename Raw4<E>::type>(card, lo.wv[j]);
     if (!SUMMARY) {
@@ -256,12 +256,20 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
 #pragma unroll
             for (int s = 0; s < O::NKC; ++s) ub[j][s] = ld_frag(sU + 16 * j * LDS_U, LDS_U, n, s * KS, g);
 
-        // S <- diag(e^gamma_C) S + Ke^T U
+        // S <- diag(e^gamma_C) S + Ke^T U; lane (g, n) takes e^gamma_C of its
+        // rows 16mt + 4g + e from the lanes that loaded them
+        f32x4 gcv[MTS];
+#pragma unroll
+        for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                gcv[mt][e] = __int_as_float(
+                    __builtin_amdgcn_ds_bpermute((16 * mt + 4 * g + e) * 4, __float_as_int(cur.gc)));
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
             for (int mt = 0; mt < MTS; ++mt) {
-                f32x4 acc = S[j][mt] * cur.gc[mt];
+                f32x4 acc = S[j][mt] * gcv[mt];
 #pragma unroll
                 for (int s = 0; s < O::NKC; ++s) acc = M::mma(cur.ke[mt][s], ub[j][s], acc);
                 S[j][mt] = acc;
