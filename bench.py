@@ -1,6 +1,6 @@
 """KDA benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-segmented] [--no-cpu-baseline]
 
 A step is one chunked prefill (update-card preparation + ordered hand-off
 with the gated read-out) of the long-prefill workload: B=1, T=65,536, H=32,
@@ -15,6 +15,9 @@ Also reported on the same JSON line:
   * the whole path against the HBM and bf16-MFMA peaks;
   * the batched decode workload (256 sequences x 32 heads, d=128, 64 steps,
     fp32 state updated in place): GB/s and fraction of HBM peak;
+  * the segmented (context-parallel) prefill of 1,048,576 tokens x 8 heads as
+    16 segments: per-call times of prepare, segment summaries, in-order
+    combine and the per-segment recompute;
   * cpu_baseline: the fp64 oracle timed on a bounded sample on the host.
 """
 from __future__ import annotations
@@ -71,6 +74,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-segmented", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -216,6 +220,63 @@ def main():
         torch.cuda.synchronize()
         result["hbm_copy_GBps"] = 2 * x.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del dd, sm, state, x, y
+        torch.cuda.empty_cache()
+
+    # --------------------------------------------------------- segmented prefill
+    if not args.no_segmented and not args.decode_only:
+        Ws = WORKLOADS[3]
+        t0 = time.time()
+        inp = workload(3)
+        log(f"[bench] generated segmented inputs in {time.time() - t0:.1f}s")
+        ds = kda.to_device(inp, dev)
+        floor_s = inp.log_alpha_min
+        del inp
+        Bs, Ts_all, Hs, nseg = Ws["B"], Ws["T"], Ws["H"], Ws["n_seg"]
+        Ts = Ts_all // nseg
+        seg = lambda x: x.view((Bs * nseg, Ts) + tuple(x.shape[2:]))
+        ps = kda.problem(Bs * nseg, Ts, Hs, D, D, kda.KDA_BF16, floor_s)
+        wss = torch.empty(kda.workspace_size(ps), dtype=torch.uint8, device=dev)
+        outs = torch.empty((Bs * nseg, Ts, Hs, D), dtype=torch.bfloat16, device=dev)
+
+        def sstep(ev=None):
+            rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+            rec(0)
+            kda.chunk_prepare(seg(ds["q"]), seg(ds["k"]), seg(ds["v"]), seg(ds["log_alpha"]), seg(ds["beta"]),
+                              floor_s, workspace=wss)
+            rec(1)
+            A, Bz = kda.segment_summarize(wss, Bs * nseg, Ts, Hs, D, torch.bfloat16, floor_s)
+            rec(2)
+            seg_in, fin = kda.segment_combine(A.view(Bs, nseg, Hs, D, D), Bz.view(Bs, nseg, Hs, D, D), None)
+            rec(3)
+            kda.chunk_scan(wss, seg(ds["g"]), floor_s, state_in=seg_in.view(Bs * nseg, Hs, D, D), out=outs,
+                           want_state=False)
+            rec(4)
+
+        sstep()
+        torch.cuda.synchronize()
+        reps = 3
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+        for r in range(reps):
+            sstep(evs[r])
+        torch.cuda.synchronize()
+        part = lambda i: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps
+        total = sum(e[0].elapsed_time(e[4]) for e in evs) / reps
+        ths = Bs * Ts_all * Hs
+        names = ("prepare", "summarize", "combine", "scan")
+        times = {nm: part(i) for i, nm in enumerate(names)}
+        log(f"[bench] segmented {total:.3f} ms (" + ", ".join(f"{k} {v:.3f}" for k, v in times.items()) + ")")
+        result["segmented"] = {
+            "workload": Ws["name"], "ms": total, "tokens_per_s": Bs * Ts_all / (total * 1e-3),
+            "ms_per_call": times,
+            # algorithmic bytes: prepare and scan as in the prefill; the
+            # summaries read the cards (1,160 B per token-head) and write
+            # 2 d^2 fp32 per segment-head; the combine reads and writes those
+            "GBps": {"prepare": PREP_BYTES * ths / (times["prepare"] * 1e-3) / 1e9,
+                     "summarize": (CARD_BYTES * ths + 2 * D * D * 4 * Bs * nseg * Hs)
+                     / (times["summarize"] * 1e-3) / 1e9,
+                     "scan": SCAN_BYTES * ths / (times["scan"] * 1e-3) / 1e9},
+        }
+        del ds, wss, outs
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- cpu baseline
