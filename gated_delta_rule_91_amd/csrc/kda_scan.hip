@@ -138,10 +138,11 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
 
 // One workgroup = NTW adjacent 16-column slices of one (batch row, head):
 // the card fragments a wave loads serve all NTW slices.
-// Depth of the operand ring (chunks of card fragments in flight per wave),
-// and how far past the ring's newest chunk the L2 prefetch runs.
-constexpr int kRing = 4;
-constexpr int kPrefetch = kRing + 1;
+// Depth of the operand ring (chunks of card fragments in flight per wave):
+// four, or three for four slices per workgroup (register file), and how far
+// past the chunk a ring load fetches the L2 prefetch runs.
+constexpr int kRing4 = 4;
+constexpr int kPrefetch = kRing4 + 1;
 
 template <typename E, int DK, int NTW, bool SUMMARY>
 __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
@@ -316,6 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     // rest (fewer than kRing full chunks, then a partial one) finish in the
     // tail from the slots already loaded.  (Named ring slots: an array of
     // them allocates worse.)
+    constexpr int kRing = NTW >= 4 ? 3 : kRing4;
     static_assert(kRing >= 2 && kRing <= 4, "ring depth");
     if (NC > 0) {
         using Full = std::integral_constant<bool, true>;
@@ -372,6 +374,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
 // one workgroup per compute unit.  Four slices exceed the register file.
 constexpr int kCUs = 256;
 inline int pick_ntw(int64_t BH, int NTALL) {
+    if (NTALL % 4 == 0 && BH * (NTALL / 4) >= kCUs) return 4;
     return (NTALL % 2 == 0 && BH * (NTALL / 2) >= kCUs) ? 2 : 1;
 }
 
@@ -390,7 +393,11 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
     if (BH == 0) return hipSuccess;
-    return pick_ntw(BH, NTALL) == 2 ? launch_scan_n<E, DK, 2, SUMMARY>(a, s) : launch_scan_n<E, DK, 1, SUMMARY>(a, s);
+    switch (pick_ntw(BH, NTALL)) {
+    case 4: return launch_scan_n<E, DK, 4, SUMMARY>(a, s);
+    case 2: return launch_scan_n<E, DK, 2, SUMMARY>(a, s);
+    default: return launch_scan_n<E, DK, 1, SUMMARY>(a, s);
+    }
 }
 
 }  // namespace

@@ -83,8 +83,9 @@ def test_f32_prefill_vs_oracle(T):
 
 # (128, 777, 5): ragged, heads not a multiple of the 8 XCDs; (64, 130, 64):
 # 128 (row, head) chains, so the hand-off runs two 16-column slices per
-# workgroup at d = 64
-@pytest.mark.parametrize("dk,T,H,mu", [(128, 777, 5, -4.0), (64, 300, 3, 0.0), (128, 64, 9, 0.0), (64, 130, 64, -4.0)])
+# workgroup at d = 64; (128, 70, 64): four slices per workgroup at d = 128
+@pytest.mark.parametrize("dk,T,H,mu", [(128, 777, 5, -4.0), (64, 300, 3, 0.0), (128, 64, 9, 0.0), (64, 130, 64, -4.0),
+                                       (128, 70, 64, -4.0)])
 def test_bf16_prefill_vs_oracle(dk, T, H, mu):
     note(f"[bf16 prefill] dk={dk} T={T} H={H}")
     inp = make_inputs(2, T, H, dk, dk, io_dtype="bf16", seed=7 + T, alpha_min=0.9, logit_mu=mu, with_state0=True)
@@ -101,6 +102,19 @@ def test_f32_d128_prefill_vs_oracle():
     workgroup in the hand-off, ragged last chunk."""
     note("[f32 prefill] dk=128 B=2 T=100 H=32")
     inp = make_inputs(2, 100, 32, 128, 128, io_dtype="f32", seed=23, alpha_min=0.9, logit_mu=-2.0, with_state0=True)
+    d = kda.to_device(inp)
+    out, st = gpu_prefill(d, inp.log_alpha_min)
+    o_ref, s_ref = oracle_run(inp)
+    eo, es = slice_err(host(out), o_ref, "out"), slice_err(host(st), s_ref, "state")
+    note(f"  rel-L2 out {eo:.2e} state {es:.2e}")
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
+
+
+def test_f32_d64_four_slices_vs_oracle():
+    """fp32 at d = 64 with 256 (row, head) chains: four 16-column slices per
+    workgroup in the hand-off (its three-deep operand ring), ragged tail."""
+    note("[f32 prefill] dk=64 B=4 T=70 H=64")
+    inp = make_inputs(4, 70, 64, 64, 64, io_dtype="f32", seed=29, alpha_min=0.9, logit_mu=-2.0, with_state0=True)
     d = kda.to_device(inp)
     out, st = gpu_prefill(d, inp.log_alpha_min)
     o_ref, s_ref = oracle_run(inp)
@@ -156,8 +170,9 @@ def test_segmented_1m_prefill_sampled_head_vs_oracle():
 
 
 # H = 4 at d = 128: 32 (row, head) chains of the augmented state, so the
-# summary runs two 16-column slices per workgroup
-@pytest.mark.parametrize("io,H", [("f32", 3), ("bf16", 3), ("bf16", 4)])
+# summary runs two 16-column slices per workgroup; H = 16: 128 chains, four
+# slices per workgroup (and the recompute too)
+@pytest.mark.parametrize("io,H", [("f32", 3), ("bf16", 3), ("bf16", 4), ("bf16", 16)])
 def test_summarize_and_combine_vs_oracle(io, H):
     note(f"[summary/combine] {io} H={H}")
     n_seg, Ts, dk = 4, 96, 64 if io == "f32" else 128
