@@ -11,16 +11,19 @@
 //   S <- diag(e^gamma_C) S + Ke^T U
 //
 // The columns of S never interact, so the chain of one (batch row, head) is
-// split into independent 16-column slices; a workgroup runs one or two of
-// them, and its state slices (d_k x 16 fp32 each) live in accumulator
-// registers for the whole sequence.  Four waves share a chain: wave w owns U/O rows 16w..16w+15 and
-// state rows w*d_k/4 .. (w+1)*d_k/4 - 1.  U and the operand copy of S cross
-// waves through LDS (two barriers per chunk); the card operands and the gate
-// values are prefetched from global memory four chunks ahead, straight into
-// registers in MFMA operand layout (a register ring, so the dependent chunk
-// loop never waits on memory latency).  Every global load is unconditional:
-// the load counter retires in order, so a load under a branch makes the
-// compiler wait for ALL outstanding loads, which would drain the ring.
+// split into independent 16-column slices; a workgroup runs one, two or four
+// of them, and its state slices (d_k x 16 fp32 each) live in accumulator
+// registers for the whole sequence.  Four waves share a chain: wave w owns
+// U/O rows 16w..16w+15 and state rows w*d_k/4 .. (w+1)*d_k/4 - 1.  U and the
+// operand copy of S cross waves through LDS (two barriers per chunk); the
+// card operands and the gate values are prefetched from global memory four
+// chunks ahead (three with four slices), straight into registers in MFMA
+// operand layout (a register ring, so the dependent chunk loop does not wait
+// on memory latency).  Every global load is unconditional: the load counter
+// retires in order, so a load under a branch makes the compiler wait for ALL
+// outstanding loads, which would drain the ring.  A wave can have at most 63
+// vector-memory operations in flight and a chunk costs it 18 loads, so the
+// ring is as deep as that allows.
 //
 // Summary mode runs the same hand-off on the augmented state [Bz | A] from
 // [0 | I]: the first d_v/16 chains carry value columns (from 0), the next
@@ -368,10 +371,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
             }
 }
 
-// Slices per workgroup: two slices share each card fragment (1.5x more work
-// per compute-unit cycle, measured on the 64K-token workload) but halve the
-// workgroup count, so they are used only when that still leaves at least
-// one workgroup per compute unit.  Four slices exceed the register file.
+// Slices per workgroup: two or four slices share each card fragment (more
+// work per compute-unit cycle) but divide the workgroup count, so the most
+// slices that still leave at least one workgroup per compute unit are used.
+// Four slices fit the register file only with a three-deep ring.
 constexpr int kCUs = 256;
 inline int pick_ntw(int64_t BH, int NTALL) {
     if (NTALL % 4 == 0 && BH * (NTALL / 4) >= kCUs) return 4;
