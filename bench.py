@@ -12,9 +12,12 @@ Also reported on the same JSON line:
   * per-kernel average durations from HIP events recorded on the launch
     stream inside the timed region, and the roofline of the dominant kernel
     (algorithmic bytes per launch / its average duration, against 8 TB/s);
-  * the whole path against the HBM and bf16-MFMA peaks;
+  * the whole path against the HBM and bf16-MFMA peaks and against the
+    attainable roofline min(MFMA peak, HBM peak x arithmetic intensity);
   * the batched decode workload (256 sequences x 32 heads, d=128, 64 steps,
-    fp32 state updated in place): GB/s and fraction of HBM peak;
+    fp32 state updated in place): GB/s and fraction of HBM peak, with a
+    plain device copy and a large bf16 GEMM timed in the same job as the
+    achievable HBM and MFMA references;
   * the segmented (context-parallel) prefill of 1,048,576 tokens x 8 heads as
     16 segments: per-call times of prepare, segment summaries, in-order
     combine and the per-segment recompute;
@@ -171,7 +174,10 @@ def main():
                   "mfma_TFLOPs": FLOP_TOK * th / (ms * 1e-3) / 1e12,
                   "mfma_frac_bf16": FLOP_TOK * th / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                   "roofline_ceiling_mfma_frac": min(1.0, FLOP_TOK / PATH_BYTES * HBM_PEAK_GBS / 1e3
-                                                    / MFMA_BF16_PEAK_TFLOPS)},
+                                                    / MFMA_BF16_PEAK_TFLOPS),
+                  # achieved FLOP rate against the attainable one, min(MFMA peak, HBM peak x intensity)
+                  "attainable_roofline_frac": FLOP_TOK * th / (ms * 1e-3) / 1e12
+                  / min(MFMA_BF16_PEAK_TFLOPS, FLOP_TOK / PATH_BYTES * HBM_PEAK_GBS / 1e3)},
         )
         del d, ws, out, st
         torch.cuda.empty_cache()
@@ -219,7 +225,20 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         result["hbm_copy_GBps"] = 2 * x.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        del dd, sm, state, x, y
+        del x, y
+        # achievable-MFMA reference in the same job: a large bf16 GEMM (library)
+        n = 8192
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b2 = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        c2 = a @ b2
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            c2 = a @ b2
+        e1.record()
+        torch.cuda.synchronize()
+        result["mfma_gemm_bf16_TFLOPs"] = 2 * n ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        del a, b2, c2, dd, sm, state
         torch.cuda.empty_cache()
 
     # --------------------------------------------------------- segmented prefill

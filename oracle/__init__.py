@@ -47,6 +47,9 @@ def _load():
         lib.kda_oracle_summary.restype = I32
         lib.kda_oracle_combine.argtypes = [I64, I32, I32, I32, I32, P, P, P, P, P]
         lib.kda_oracle_combine.restype = I32
+        lib.kda_oracle_grad.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, P, P, F64, P, P, P,
+                                        P, P, P, P, P, P, P, I32]
+        lib.kda_oracle_grad.restype = I32
         _lib = lib
     return _lib
 
@@ -111,3 +114,23 @@ def kda_combine(A, Bz, state_init=None) -> Tuple[np.ndarray, np.ndarray]:
     if rc != 0:
         raise RuntimeError(f"kda_oracle_combine failed ({rc})")
     return seg_in, fin
+
+
+def kda_grad(q, k, v, log_alpha, beta, g, log_alpha_min: float, state0=None, d_out=None, d_state=None,
+             nthreads: Optional[int] = None) -> dict:
+    """Gradients of <d_out, out> + <d_state, final state> (fp64 adjoint of the
+    step recurrence).  Returns a dict with dq, dk, dv, dlog_alpha, dbeta, dg
+    (shapes of the inputs) and dstate0 [B,H,dk,dv]."""
+    q, k, v, la, bt, g, s0, do, ds = map(_c, (q, k, v, log_alpha, beta, g, state0, d_out, d_state))
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    r = {n: np.zeros(x.shape) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dlog_alpha", la), ("dbeta", bt),
+                                          ("dg", g))}
+    r["dstate0"] = np.zeros((B, H, dk, dv))
+    rc = _load().kda_oracle_grad(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(la), _p(bt), _p(g),
+                                 float(log_alpha_min), _p(s0), _p(do), _p(ds),
+                                 _p(r["dq"]), _p(r["dk"]), _p(r["dv"]), _p(r["dlog_alpha"]), _p(r["dbeta"]),
+                                 _p(r["dg"]), _p(r["dstate0"]), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_grad failed ({rc})")
+    return r

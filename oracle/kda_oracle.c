@@ -43,6 +43,13 @@
  *   kda_oracle_combine: the in-order prefix merge of those pairs (same
  *   paragraph): S_in(0) = S_init, S_in(n+1) = A_n S_in(n) + Bz_n.
  *
+ *   kda_oracle_grad: the gradients of L = <d_out, out> + <d_state, S_T> with
+ *   respect to q, k, v, log_alpha, beta, g and the initial state -- the
+ *   adjoint of the four steps above, taken token by token in reverse (the
+ *   backward pass serves training [zuoshipin §四: FlashKDA serves training
+ *   throughput]).  The forward pass stores the state entering every token;
+ *   each reverse step recomputes that token's intermediates from it.
+ *
  * All arrays are fp64, C-contiguous, token-major [B,T,H,d]; states are
  * [B,H,d_k,d_v] with row = key channel.  Work items are (b, h, block of state
  * columns): the columns of S never interact, so a block of them can be
@@ -275,4 +282,214 @@ int kda_oracle_combine(int64_t B, int n_seg, int H, int dk, int dv,
         }
     free(cur); free(nxt);
     return 0;
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* Gradients (the adjoint of the step recurrence, one (b, h) per work item). */
+
+typedef struct {
+    int64_t B, T;
+    int H, dk, dv;
+    const double *q, *k, *v, *log_alpha, *beta, *g, *state_in, *d_out, *d_state;
+    double log_alpha_min;
+    double *dq, *dk_, *dv_, *dla, *dbeta, *dg, *d_state_in;
+} gjob_t;
+
+typedef struct {
+    const gjob_t *job;
+    int64_t first, step, count;
+    int status;
+} gworker_t;
+
+/* x^ = x / max(|x|, 1e-6); returns the divisor */
+static double unit(const double *x, double *xh, int n)
+{
+    double s = 0.0;
+    for (int c = 0; c < n; ++c) s += x[c] * x[c];
+    s = sqrt(s);
+    const double nx = s < 1e-6 ? 1e-6 : s;
+    for (int c = 0; c < n; ++c) xh[c] = x[c] / nx;
+    return s;
+}
+
+/* dx from dx^ for x^ = x / max(|x|, 1e-6): below the floor the divisor is a
+ * constant; above it, d(x/|x|) = (I - x^ x^T) / |x|. */
+static void unit_back(const double *xh, double norm, const double *dxh, double *dx, int n)
+{
+    if (norm < 1e-6) {
+        for (int c = 0; c < n; ++c) dx[c] = dxh[c] / 1e-6;
+        return;
+    }
+    double dot = 0.0;
+    for (int c = 0; c < n; ++c) dot += xh[c] * dxh[c];
+    for (int c = 0; c < n; ++c) dx[c] = (dxh[c] - xh[c] * dot) / norm;
+}
+
+static int grad_item(const gjob_t *J, int64_t b, int h)
+{
+    const int dk = J->dk, dv = J->dv, H = J->H;
+    const int64_t T = J->T;
+    const size_t SZ = (size_t)dk * dv;
+    double *hist = (double *)malloc((size_t)(T > 0 ? T : 1) * SZ * sizeof(double)); /* state entering token t */
+    double *S = (double *)malloc(SZ * sizeof(double));
+    double *Sp = (double *)malloc(SZ * sizeof(double));   /* retained state D S_prev */
+    double *dS = (double *)malloc(SZ * sizeof(double));
+    double *work = (double *)malloc((size_t)(8 * dk + 8 * dv) * sizeof(double));
+    if (!hist || !S || !Sp || !dS || !work) { free(hist); free(S); free(Sp); free(dS); free(work); return 1; }
+    double *kh = work, *qh = kh + dk, *D = qh + dk, *dkh = D + dk, *dqh = dkh + dk, *tmpk = dqh + dk;
+    double *p = tmpk + 2 * dk, *u = p + dv, *o = u + dv, *du = o + dv, *dp = du + dv, *dov = dp + dv;
+    const size_t sb = ((size_t)b * H + h) * SZ;
+
+    for (size_t i = 0; i < SZ; ++i) S[i] = J->state_in ? J->state_in[sb + i] : 0.0;
+    /* forward: the same four steps as run_item, keeping the entering states */
+    for (int64_t t = 0; t < T; ++t) {
+        const size_t row = ((size_t)b * (size_t)T + (size_t)t) * (size_t)H + (size_t)h;
+        memcpy(hist + (size_t)t * SZ, S, SZ * sizeof(double));
+        for (int c = 0; c < dk; ++c) {
+            const double la = J->log_alpha[row * dk + c];
+            const double a = exp(la > J->log_alpha_min ? la : J->log_alpha_min);
+            for (int j = 0; j < dv; ++j) S[(size_t)c * dv + j] *= a;
+        }
+        unit(J->k + row * dk, kh, dk);
+        for (int j = 0; j < dv; ++j) {
+            double pj = 0.0;
+            for (int c = 0; c < dk; ++c) pj += S[(size_t)c * dv + j] * kh[c];
+            const double uj = J->beta[row] * (J->v[row * dv + j] - pj);
+            for (int c = 0; c < dk; ++c) S[(size_t)c * dv + j] += kh[c] * uj;
+        }
+    }
+
+    /* reverse: dS is the gradient with respect to the state after token t */
+    for (size_t i = 0; i < SZ; ++i) dS[i] = J->d_state ? J->d_state[sb + i] : 0.0;
+    for (int64_t t = T - 1; t >= 0; --t) {
+        const size_t row = ((size_t)b * (size_t)T + (size_t)t) * (size_t)H + (size_t)h;
+        const double *Sprev = hist + (size_t)t * SZ;
+        const double bt = J->beta[row];
+        const double *vt = J->v + row * dv, *gt = J->g + row * dv;
+        /* recompute the token's intermediates */
+        for (int c = 0; c < dk; ++c) {
+            const double la = J->log_alpha[row * dk + c];
+            D[c] = exp(la > J->log_alpha_min ? la : J->log_alpha_min);
+            for (int j = 0; j < dv; ++j) Sp[(size_t)c * dv + j] = D[c] * Sprev[(size_t)c * dv + j];
+        }
+        const double nk = unit(J->k + row * dk, kh, dk);
+        const double nq = unit(J->q + row * dk, qh, dk);
+        for (int j = 0; j < dv; ++j) {
+            double pj = 0.0;
+            for (int c = 0; c < dk; ++c) pj += Sp[(size_t)c * dv + j] * kh[c];
+            p[j] = pj;
+            u[j] = bt * (vt[j] - pj);
+        }
+        for (int c = 0; c < dk; ++c)      /* S = state after the token */
+            for (int j = 0; j < dv; ++j) S[(size_t)c * dv + j] = Sp[(size_t)c * dv + j] + kh[c] * u[j];
+        for (int j = 0; j < dv; ++j) {
+            double oj = 0.0;
+            for (int c = 0; c < dk; ++c) oj += S[(size_t)c * dv + j] * qh[c];
+            o[j] = oj;
+        }
+        /* 4. out = o * sigmoid(g), o = S^T qh */
+        for (int j = 0; j < dv; ++j) {
+            const double dy = J->d_out ? J->d_out[row * dv + j] : 0.0;
+            const double sg = 1.0 / (1.0 + exp(-gt[j]));
+            dov[j] = dy * sg;
+            J->dg[row * dv + j] = dy * o[j] * sg * (1.0 - sg);
+        }
+        for (int c = 0; c < dk; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += S[(size_t)c * dv + j] * dov[j];
+                dS[(size_t)c * dv + j] += qh[c] * dov[j];
+            }
+            dqh[c] = acc;
+        }
+        /* 3. S = Sp + kh u^T, u = beta (v - p), p = Sp^T kh */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += dS[(size_t)c * dv + j] * kh[c];
+            du[j] = acc;
+        }
+        double db = 0.0;
+        for (int j = 0; j < dv; ++j) {
+            db += du[j] * (vt[j] - p[j]);
+            J->dv_[row * dv + j] = bt * du[j];
+            dp[j] = -bt * du[j];
+        }
+        J->dbeta[row] = db;
+        for (int c = 0; c < dk; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                acc += dS[(size_t)c * dv + j] * u[j] + Sp[(size_t)c * dv + j] * dp[j];
+                dS[(size_t)c * dv + j] += kh[c] * dp[j];      /* now the gradient w.r.t. Sp */
+            }
+            dkh[c] = acc;
+        }
+        /* 1. Sp = diag(exp(lambda)) S_prev, lambda = max(log_alpha, floor) */
+        for (int c = 0; c < dk; ++c) {
+            double dl = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                dl += Sp[(size_t)c * dv + j] * dS[(size_t)c * dv + j];
+                dS[(size_t)c * dv + j] *= D[c];                 /* now the gradient w.r.t. S_prev */
+            }
+            const double la = J->log_alpha[row * dk + c];
+            J->dla[row * dk + c] = la > J->log_alpha_min ? dl : 0.0;
+        }
+        /* 2. normalisations */
+        unit_back(kh, nk, dkh, J->dk_ + row * dk, dk);
+        unit_back(qh, nq, dqh, J->dq + row * dk, dk);
+    }
+    if (J->d_state_in) memcpy(J->d_state_in + sb, dS, SZ * sizeof(double));
+    free(hist); free(S); free(Sp); free(dS); free(work);
+    return 0;
+}
+
+static void *gworker_main(void *arg)
+{
+    gworker_t *W = (gworker_t *)arg;
+    const gjob_t *J = W->job;
+    for (int64_t n = 0; n < W->count; ++n) {
+        const int64_t bh = W->first + n * W->step;
+        if (grad_item(J, bh / J->H, (int)(bh % J->H))) { W->status = 1; return NULL; }
+    }
+    return NULL;
+}
+
+/* Gradients of L = <d_out, out> + <d_state, S_T> (either may be NULL = 0).
+ * Outputs have the shapes of the inputs; d_state_in may be NULL. */
+int kda_oracle_grad(int64_t B, int64_t T, int H, int dk, int dv,
+                    const double *q, const double *k, const double *v,
+                    const double *log_alpha, const double *beta, const double *g,
+                    double log_alpha_min, const double *state_in,
+                    const double *d_out, const double *d_state,
+                    double *dq, double *dk_, double *dv_, double *dla, double *dbeta, double *dg,
+                    double *d_state_in, int nthreads)
+{
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return 2;
+    gjob_t J;
+    memset(&J, 0, sizeof J);
+    J.B = B; J.T = T; J.H = H; J.dk = dk; J.dv = dv;
+    J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = beta; J.g = g;
+    J.log_alpha_min = log_alpha_min; J.state_in = state_in; J.d_out = d_out; J.d_state = d_state;
+    J.dq = dq; J.dk_ = dk_; J.dv_ = dv_; J.dla = dla; J.dbeta = dbeta; J.dg = dg; J.d_state_in = d_state_in;
+    const int64_t items = B * (int64_t)H;
+    if (items == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > items) nthreads = (int)items;
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    gworker_t *ws = (gworker_t *)calloc((size_t)nthreads, sizeof(gworker_t));
+    if (!th || !ws) { free(th); free(ws); return 1; }
+    int started = 0, status = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        ws[i].job = &J;
+        ws[i].first = i;
+        ws[i].step = nthreads;
+        ws[i].count = (items - i + nthreads - 1) / nthreads;
+        if (nthreads == 1) { gworker_main(&ws[i]); continue; }
+        if (pthread_create(&th[i], NULL, gworker_main, &ws[i]) != 0) { status = 1; break; }
+        ++started;
+    }
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i) status |= ws[i].status;
+    free(th); free(ws);
+    return status;
 }
