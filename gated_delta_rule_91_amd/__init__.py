@@ -8,7 +8,7 @@ CPU or PyTorch fallback: if the library is missing, every call raises.
 
 Entry points (same names as the C ABI, minus the ``kda_`` prefix):
     workspace_size, chunk_prepare, chunk_scan, segment_summarize,
-    segment_combine, decode_step
+    segment_combine, decode_step, backward_workspace_size, backward
 Conveniences built from them: prefill, segmented_prefill.
 """
 from __future__ import annotations
@@ -25,7 +25,8 @@ KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "workspace too small",
           4: "HIP runtime error"}
 EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_segment_summarize",
-           "kda_segment_combine", "kda_decode_step", "kda_status_string")
+           "kda_segment_combine", "kda_decode_step", "kda_backward_workspace_size", "kda_backward",
+           "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -59,8 +60,12 @@ def lib() -> ctypes.CDLL:
         L.kda_segment_summarize.argtypes = [PP, P, SZ, P, P, P]
         L.kda_segment_combine.argtypes = [I64, I32, I32, I32, I32, P, P, P, P, P, P]
         L.kda_decode_step.argtypes = [I64, I32, I32, I32, I32, F32, P, P, P, P, P, P, P, P, P]
+        L.kda_backward_workspace_size.argtypes = [PP]
+        L.kda_backward_workspace_size.restype = SZ
+        L.kda_backward.argtypes = [PP] + [P] * 16 + [P, SZ, P]
         for f in EXPORTS[1:-1]:
-            getattr(L, f).restype = I32
+            if f != "kda_backward_workspace_size":
+                getattr(L, f).restype = I32
         L.kda_status_string.argtypes = [I32]
         L.kda_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -186,6 +191,36 @@ def decode_step(q, k, v, log_alpha, beta, g, state, log_alpha_min: float, out=No
         N, H, dk, dv, _io_code(q.dtype), float(log_alpha_min), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
         _ptr(beta), _ptr(g), _ptr(state), _ptr(out), _stream(stream)))
     return out
+
+
+def backward_workspace_size(p: KdaProblem) -> int:
+    n = lib().kda_backward_workspace_size(ctypes.byref(p))
+    if n == 0 and p.batch * p.heads * p.seqlen > 0:
+        raise KdaError("kda_backward_workspace_size", 2)
+    return n
+
+
+def backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, d_out=None, d_state=None,
+             want_dstate: bool = True, workspace=None, stream=None) -> dict:
+    """Gradients of <d_out, out> + <d_state, final state> with respect to every
+    input of prefill.  Returns a dict with dq, dk, dv, dg (dtype of q), dlog_alpha,
+    dbeta (fp32) and dstate0 ([B,H,dk,dv] fp32, None unless want_dstate)."""
+    torch = _torch()
+    p = _problem_of(q, v, log_alpha_min)
+    B, T, H, dk = q.shape
+    nbytes = backward_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    r = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+             dlog_alpha=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta))
+    r["dstate0"] = torch.empty((B, H, dk, v.shape[-1]), dtype=torch.float32, device=q.device) if want_dstate \
+        else None
+    _check("kda_backward", lib().kda_backward(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g), _ptr(state_in),
+        _ptr(d_out), _ptr(d_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dlog_alpha"]),
+        _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return r
 
 
 def prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, workspace=None, stream=None):

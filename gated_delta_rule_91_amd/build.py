@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_prepare.hip", "kda_scan.hip", "kda_decode.hip", "kda_combine.hip"]
+SOURCES = ["kda_api.hip", "kda_prepare.hip", "kda_scan.hip", "kda_decode.hip", "kda_combine.hip", "kda_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

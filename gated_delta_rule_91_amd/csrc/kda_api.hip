@@ -168,4 +168,35 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
     return hip_status(launch_decode(io_dtype == KDA_BF16, dk, a, (hipStream_t)stream));
 }
 
+size_t kda_backward_workspace_size(const kda_problem* p) {
+    if (check_problem(p) != KDA_OK || p->seqlen == 0) return 0;
+    return backward_workspace_bytes(p->batch, p->seqlen, p->heads, p->dk);
+}
+
+kda_status kda_backward(const kda_problem* p, const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const void* g, const float* state_in, const void* d_out,
+                        const float* d_state, void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
+                        void* dg, float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->batch > 0 && p->seqlen > 0;
+    if (!ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) || !ok_ptr(log_alpha, tokens) ||
+        !ok_beta(beta, tokens) || !ok_ptr(g, tokens) || !ok_ptr(dq, tokens) || !ok_ptr(dk, tokens) ||
+        !ok_ptr(dv, tokens) || !ok_ptr(dlog_alpha, tokens) || !ok_beta(dbeta, tokens) || !ok_ptr(dg, tokens) ||
+        !ok_ptr(workspace, tokens) || !ok_opt_ptr(state_in) || !ok_opt_ptr(d_out) || !ok_opt_ptr(d_state) ||
+        !ok_opt_ptr(d_state_in))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_backward_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (p->batch == 0 || (!tokens && !d_state_in)) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.g = g; a.state_in = state_in;
+    a.d_out = d_out; a.d_state = d_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dg = dg;
+    a.d_state_in = d_state_in;
+    a.ws = static_cast<float*>(workspace);
+    a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.floor_ = p->log_alpha_min;
+    return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, (hipStream_t)stream));
+}
+
 }  // extern "C"

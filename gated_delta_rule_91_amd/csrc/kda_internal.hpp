@@ -57,7 +57,32 @@ struct CombineArgs {
     int n_seg, H, dk, dv;
 };
 
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const void* g;
+    const float* state_in;   // [B,H,dk,dv] or null
+    const void* d_out;       // [B,T,H,dv] io dtype, or null (zero)
+    const float* d_state;    // [B,H,dk,dv] or null (zero)
+    void* dq;                // [B,T,H,dk] io dtype
+    void* dk;
+    void* dv;                // [B,T,H,dv] io dtype
+    float* dlog_alpha;       // [B,T,H,dk]
+    float* dbeta;            // [B,T,H]
+    void* dg;                // [B,T,H,dv] io dtype
+    float* d_state_in;       // [B,H,dk,dv] or null
+    float* ws;               // backward_workspace_bytes
+    int64_t B, T;
+    int H;
+    float floor_;
+};
+
 size_t card_bytes(bool bf16, int dk);
+size_t backward_workspace_bytes(int64_t B, int64_t T, int H, int dk);
+hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t s);
 hipError_t launch_prepare(bool bf16, int dk, const PrepareArgs& a, hipStream_t s);
 hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s);
 hipError_t launch_decode(bool bf16, int dk, const DecodeArgs& a, hipStream_t s);

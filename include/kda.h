@@ -129,6 +129,32 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
                            const float* log_alpha, const float* beta, const void* g,
                            float* state, void* out, void* stream);
 
+/* Bytes of scratch kda_backward needs for problem p: the state entering every
+ * chunk plus the 64 states entering one chunk's tokens, fp32, per (b, h).
+ * Returns 0 if p is invalid or unsupported, or if p has no tokens. */
+size_t kda_backward_workspace_size(const kda_problem* p);
+
+/* Gradients for training [zuoshipin.com/article/18261 §四: the fused kernels
+ * serve training throughput as well as inference; the recurrence is the one
+ * at the top of this file, zuoshipin §二].  With
+ *   L = <d_out, out> + <d_state, S_T>,
+ * out and S_T being what kda_chunk_prepare + kda_chunk_scan compute from the
+ * same inputs, writes dL/dq, dL/dk, dL/dv, dL/dlog_alpha, dL/dbeta, dL/dg and
+ * dL/dstate_in.  Where log_alpha <= log_alpha_min the floor binds and
+ * dlog_alpha is 0; where |k_t| or |q_t| is below 1e-6 the normaliser is the
+ * constant 1e-6.
+ *   q, k, v, log_alpha, beta, g, state_in: as for prefill (state_in may be NULL)
+ *   d_out: [B,T,H,dv] io_dtype, or NULL (zero);  d_state: [B,H,dk,dv] fp32, or NULL
+ *   dq, dk: [B,T,H,dk], dv, dg: [B,T,H,dv] io_dtype;  dlog_alpha: [B,T,H,dk] fp32;
+ *   dbeta: [B,T,H] fp32 (4-byte alignment suffices);  d_state_in: [B,H,dk,dv] fp32,
+ *   or NULL.  Every output is overwritten, not accumulated.
+ *   workspace: >= kda_backward_workspace_size(p) bytes (contents on entry unused). */
+kda_status kda_backward(const kda_problem* p, const void* q, const void* k, const void* v,
+                        const float* log_alpha, const float* beta, const void* g, const float* state_in,
+                        const void* d_out, const float* d_state, void* dq, void* dk, void* dv,
+                        float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* kda_status_string(kda_status s);
 

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -111,12 +111,44 @@ def test_scan_summarize_combine_decode_argument_errors(L):
     assert dec(N=0, q=None, k=None, v=None, la=None, b=None, g=None, s=None, o=None) == 0
 
 
+def _bwd(L, pr, ws, **kw):
+    names = ["q", "k", "v", "la", "b", "g", "s0", "do", "ds", "dq", "dk", "dv", "dla", "db", "dg", "ds0", "w"]
+    vals = {n: FAKE for n in names}
+    vals.update(s0=None, do=FAKE, ds=None, ds0=FAKE)
+    vals.update(kw)
+    n = kw.get("n", ws)
+    return L.kda_backward(ctypes.byref(pr) if pr is not None else None, *[vals[x] for x in names], n, None)
+
+
+def test_backward_workspace_and_argument_errors(L):
+    p = _p()
+    ws = L.kda_backward_workspace_size(ctypes.byref(p))
+    # per (b, h): 4 chunk checkpoints + 64 entering states, 128 x 128 fp32 each
+    assert ws == 2 * 3 * (4 + 64) * 128 * 128 * 4
+    assert L.kda_backward_workspace_size(ctypes.byref(_p(seqlen=0))) == 0
+    assert L.kda_backward_workspace_size(ctypes.byref(_p(dk=96, dv=96))) == 0
+    assert _bwd(L, None, ws) == 1
+    assert _bwd(L, p, ws, q=None) == 1
+    assert _bwd(L, p, ws, dla=None) == 1
+    assert _bwd(L, p, ws, dg=MISALIGNED) == 1
+    assert _bwd(L, p, ws, do=MISALIGNED) == 1
+    assert _bwd(L, p, ws, w=None) == 1
+    assert _bwd(L, p, ws, n=ws - 1) == 3
+    assert _bwd(L, _p(dk=64, dv=128), ws) == 2
+    assert _bwd(L, _p(log_alpha_min=0.5), ws) == 1
+    # nothing to do: no rows, or no tokens and no state gradient wanted
+    none = {n: None for n in ["q", "k", "v", "la", "b", "g", "dq", "dk", "dv", "dla", "db", "dg", "w"]}
+    assert _bwd(L, _p(batch=0), 0, ds0=None, **none) == 0
+    assert _bwd(L, _p(seqlen=0), 0, ds0=None, **none) == 0
+
+
 @pytest.mark.skipif(_have_gpu(), reason="only meaningful where no HIP device exists")
 def test_valid_call_without_device_reports_hip_error(L):
     p = _p()
     ws = L.kda_workspace_size(ctypes.byref(p))
     assert L.kda_chunk_prepare(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 4
     assert L.kda_decode_step(4, 2, 128, 128, 1, -0.1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert _bwd(L, p, L.kda_backward_workspace_size(ctypes.byref(p))) == 4
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -1,0 +1,132 @@
+"""kda_backward (HIP) vs the fp64 oracle adjoint, element by element (needs an
+MI355X).
+
+Same inputs on both sides (bf16 -> fp64 is exact).  Error measure: relative
+L2 per (batch row, head) slice of every gradient; the largest must stay
+within 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (there dq, dk, dv and dg
+are rounded to bf16 on output, half an ulp = 2e-3 relative).  q and k are
+scaled by 0.5 and 2 (exact in both dtypes) so the normalisation's 1/|x|
+factor is exercised, and one key row is zero (the 1e-6 normaliser branch).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from kda_inputs import f32_to_bf16_bits, make_inputs, to_f64
+
+torch = pytest.importorskip("torch")
+import gated_delta_rule_91_amd as kda
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda"
+TOKEN_GRADS = ("dq", "dk", "dv", "dg", "dlog_alpha", "dbeta")
+
+
+def note(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def slice_err(gpu, ref, token_major=True):
+    """max rel-L2 over (b, h) slices of [B,T,H,...] (or [B,H,...] states)."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if token_major:
+        gpu, ref = np.moveaxis(gpu, 2, 1), np.moveaxis(ref, 2, 1)
+    B, H = ref.shape[:2]
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            d = np.linalg.norm((gpu[b, h] - ref[b, h]).ravel())
+            n = np.linalg.norm(ref[b, h].ravel())
+            worst = max(worst, d / n if n > 0 else d)
+    return worst
+
+
+def _io(a64, io_dtype):
+    """(array in the I/O dtype's storage, its exact fp64 value)."""
+    if io_dtype == "bf16":
+        bits = f32_to_bf16_bits(a64.astype(np.float32))
+        return bits, to_f64(bits, "bf16")
+    a = a64.astype(np.float32)
+    return a, a.astype(np.float64)
+
+
+def _dev(a, io_dtype):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _case(B, T, H, d, io_dtype, seed, *, state0=True, d_out=True, d_state=True, zero_key=True, alpha_min=0.9):
+    inp = make_inputs(B, T, H, d, d, io_dtype=io_dtype, seed=seed, alpha_min=alpha_min, logit_mu=-1.0,
+                      with_state0=state0)
+    f = lambda a: to_f64(a, io_dtype)
+    q64, k64 = f(inp.q) * 0.5, f(inp.k) * 2.0
+    if zero_key and T > 5:
+        k64[0, 5, 0, :] = 0.0
+    rng = np.random.default_rng(seed + 1000)
+    q_io, q64 = _io(q64, io_dtype)
+    k_io, k64 = _io(k64, io_dtype)
+    do_io, do64 = _io(rng.standard_normal((B, T, H, d)), io_dtype) if d_out else (None, None)
+    ds = rng.standard_normal((B, H, d, d)).astype(np.float32) if d_state else None
+    ref = oracle.kda_grad(q64, k64, f(inp.v), inp.log_alpha, inp.beta, f(inp.g), inp.log_alpha_min, inp.state0,
+                          d_out=do64, d_state=ds)
+    t = dict(q=_dev(q_io, io_dtype), k=_dev(k_io, io_dtype), v=_dev(inp.v, io_dtype), g=_dev(inp.g, io_dtype),
+             log_alpha=_dev(inp.log_alpha, "f32"), beta=_dev(inp.beta, "f32"))
+    note(f"[backward] B={B} T={T} H={H} d={d} {io_dtype} seed={seed} state0={state0} d_out={d_out} "
+         f"d_state={d_state}")
+    gr = kda.backward(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["g"], inp.log_alpha_min,
+                      state_in=None if inp.state0 is None else _dev(inp.state0, "f32"),
+                      d_out=None if do_io is None else _dev(do_io, io_dtype),
+                      d_state=None if ds is None else _dev(ds, "f32"))
+    torch.cuda.synchronize()
+    return gr, ref
+
+
+def _check(gr, ref, io_dtype):
+    errs = {n: slice_err(gr[n].float().cpu().numpy(), ref[n]) for n in TOKEN_GRADS}
+    errs["dstate0"] = slice_err(gr["dstate0"].cpu().numpy(), ref["dstate0"], token_major=False)
+    note("  rel-L2 " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[io_dtype], (n, e)
+
+
+@pytest.mark.parametrize("T", [130, 64, 1])
+def test_f32_d64_backward_vs_oracle(T):
+    gr, ref = _case(2, T, 3, 64, "f32", seed=500 + T)
+    _check(gr, ref, "f32")
+
+
+def test_f32_d128_backward_vs_oracle():
+    gr, ref = _case(1, 200, 2, 128, "f32", seed=611)
+    _check(gr, ref, "f32")
+
+
+@pytest.mark.parametrize("B,T,H,d", [(2, 130, 3, 64), (1, 300, 4, 128)])
+def test_bf16_backward_vs_oracle(B, T, H, d):
+    gr, ref = _case(B, T, H, d, "bf16", seed=700 + T)
+    _check(gr, ref, "bf16")
+
+
+def test_backward_without_optional_inputs():
+    """No initial state and no output gradient: only the final-state seed
+    drives the gradients (q and g then get exactly zero)."""
+    gr, ref = _case(1, 100, 2, 64, "f32", seed=801, state0=False, d_out=False)
+    _check(gr, ref, "f32")
+    assert torch.count_nonzero(gr["dq"]).item() == 0 and torch.count_nonzero(gr["dg"]).item() == 0
+
+
+def test_backward_without_state_seed():
+    gr, ref = _case(2, 70, 2, 64, "bf16", seed=802, d_state=False)
+    _check(gr, ref, "bf16")
+
+
+def test_backward_empty_sequence_passes_state_seed_through():
+    ds = torch.randn(2, 3, 64, 64, device=DEV)
+    e = torch.empty(2, 0, 3, 64, device=DEV)
+    gr = kda.backward(e, e, e, e, torch.empty(2, 0, 3, device=DEV), e, -0.1, d_state=ds)
+    torch.cuda.synchronize()
+    assert torch.equal(gr["dstate0"], ds)
