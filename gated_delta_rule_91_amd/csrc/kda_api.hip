@@ -170,7 +170,7 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
 
 size_t kda_backward_workspace_size(const kda_problem* p) {
     if (check_problem(p) != KDA_OK || p->seqlen == 0) return 0;
-    return backward_workspace_bytes(p->batch, p->seqlen, p->heads, p->dk);
+    return backward_workspace_bytes(p->io_dtype == KDA_BF16, p->batch, p->seqlen, p->heads, p->dk);
 }
 
 kda_status kda_backward(const kda_problem* p, const void* q, const void* k, const void* v, const float* log_alpha,
@@ -194,8 +194,8 @@ kda_status kda_backward(const kda_problem* p, const void* q, const void* k, cons
     a.d_out = d_out; a.d_state = d_state;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dg = dg;
     a.d_state_in = d_state_in;
-    a.ws = static_cast<float*>(workspace);
-    a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.floor_ = p->log_alpha_min;
+    a.ws = static_cast<char*>(workspace);
+    a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p); a.floor_ = p->log_alpha_min;
     return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, (hipStream_t)stream));
 }
 

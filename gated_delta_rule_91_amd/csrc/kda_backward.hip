@@ -1,30 +1,39 @@
-// kda_backward.hip -- gradients of the KDA token mixer for training: with
-// L = <d_out, out> + <d_state, S_T>, the gradients with respect to q, k, v,
-// log_alpha, beta, g and the initial state (the pages say the fast kernels
-// serve training throughput [zuoshipin.com/article/18261 §四, FlashKDA
-// paragraph]; the recurrence is the one of the forward path, §二).
+// kda_backward.hip -- gradients of the KDA token mixer for training, by the
+// chunk method run in reverse (the pages say the fused chunk kernels serve
+// training throughput [zuoshipin.com/article/18261 §四, FlashKDA paragraph];
+// the recurrence is the one of the forward path, §二).
 //
-// This is the token-recurrent form of the adjoint, in fp32, one workgroup
-// per (batch row, head):
-//   phase 1  the forward recurrence over the whole sequence, storing the
-//            state entering every chunk of 64 tokens (checkpoints);
-//   phase 2  the chunks in reverse: the chunk's 64 entering states are
-//            recomputed from its checkpoint into the workspace, then its
-//            tokens are walked backwards.  Per token, with S_prev the entering
-//            state, D = diag(e^lambda), S' = D S_prev, p = S'^T kh,
-//            u = beta (v - p), S = S' + kh u^T, o = S^T qh, and dS the
-//            gradient with respect to S:
-//              do = d_out * sigmoid(g);  dg = d_out * o * sigmoid'(g)
-//              dqh = S do;  dS += qh do^T
-//              du = dS^T kh;  dbeta = du . (v - p);  dv = beta du;  dp = -beta du
-//              dkh = dS u + S' dp;  dS' = dS + kh dp^T
-//              dlambda_c = sum_j S'[c][j] dS'[c][j] (zero where the floor binds)
-//              dS_prev = D dS';  dk, dq from dkh, dqh through the L2 normalisation
+// With L = <d_out, out> + <d_state, S_T>, inside one chunk (C = 64 tokens,
+// S0 the state entering it, dS the gradient of the state leaving it) the
+// forward is
+//   A  = strict_lower(Kt Kh^T),  P = lower_incl(Qt Kh^T),  T = (I + diag(beta) A)^-1
+//   R  = V - Kt S0,  U = T diag(beta) R,  O = Qt S0 + P U,  out = O * sigmoid(g)
+//   S_C = G S0 + Ke^T U,  G = diag(e^gamma_C)
+// (Kt, Kh, Qt, Ke: k^ and q^ with the per-channel decay folded in, as in the
+// prepare kernel), so its adjoint is
+//   dO = d_out * sigmoid(g),  dg = d_out * out * (1 - sigmoid(g))
+//   dU = Ke dS + P^T dO,  dU~ = T^T dU,  dv = diag(beta) dU~
+//   dM = -dU~ U^T,  dbeta_i = dU~_i . R_i + sum_j dM_ij A_ij,  dA = strict_lower(diag(beta) dM)
+//   dP = lower_incl(dO U^T)
+//   dQt = dO S0^T + dP Kh,  dKt = -(diag(beta) dU~) S0^T + dA Kh,  dKh = dP^T Qt + dA^T Kt,
+//   dKe = U dS^T,  dgamma_C += rowsum(S0 * dS) e^gamma_C + sum_i dKe_i * Ke_i
+//   dS0 = G dS + Qt^T dO - Wk^T dU        (Wk = T diag(beta) Kt)
+// and dgamma_i, dk^, dq^ follow from the decay folding; dlog_alpha is the
+// reverse cumulative sum of dgamma over the chunk (zero where the floor
+// binds), and dk, dq come through the L2 normalisation.
 //
-// Thread (column group cg, row group rg) keeps an RPT x 4 block of the state
-// and of its gradient in registers.  Column sums over the rows go through
-// LDS (one barrier each); row sums over the columns are lane shuffles inside
-// the wave (a wave holds whole rows).
+// Kernels, in order (the first two are the forward path's own):
+//   1. kda_prepare_kernel     forward update cards
+//   2. kda_scan_kernel        forward hand-off, also storing the state that
+//                             enters every chunk (and out, for dg)
+//   3. kda_bwd_card_kernel    per chunk, in parallel: the operands of the
+//                             reverse hand-off -- Ke, Qt^T, -Wk^T, dO in MFMA
+//                             operand order and P^T dO in accumulator order
+//   4. kda_bwd_scan_kernel    the reverse hand-off dS <- G dS + Qt^T dO - Wk^T dU
+//                             over the chunks in reverse, one workgroup per
+//                             16-column slice; stores the dS leaving every chunk
+//   5. kda_bwd_grad_kernel    per chunk, in parallel: every token gradient
+//                             from S0, dS and the chunk's inputs (fp32 MFMA)
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -32,252 +41,712 @@ namespace kda {
 
 namespace {
 
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The operands of the reverse hand-off for one (batch row, head, chunk):
+//   KEA [C x DK]  Ke in A-fragment order          (dU = Ke dS + ...)
+//   QTT [DK x C]  Qt^T in A-fragment order        (dS += Qt^T dO)
+//   WKT [DK x C]  -Wk^T in A-fragment order       (dS += -Wk^T dU)
+//   DOT [DV x C]  dO^T in A-fragment order, which is dO in B-fragment order
+//   DUL [C x DV]  P^T dO in accumulator order (the layout of Wv in Card)
+//   G   [DK]      e^gamma_C, fp32
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads) void kda_backward_kernel(BackwardArgs a) {
-    constexpr int DV = DK;
-    constexpr int C = kChunk;
-    constexpr int CG = DV / 4;          // 4-column groups
-    constexpr int RG = kThreads / CG;   // row groups
-    constexpr int RPT = DK / RG;        // rows per thread
-    constexpr int EPL = DK / 64;        // elements per lane for the norm sweep
-    static_assert(64 % CG == 0, "a wave holds whole rows");
-    static_assert(RPT <= CG, "lane cg == i writes row i of the thread's block");
+struct BCard {
+    static constexpr int C = kChunk;
+    static constexpr size_t KEA = 0;
+    static constexpr size_t QTT = KEA + (size_t)C * DK * sizeof(E);
+    static constexpr size_t WKT = QTT + (size_t)DK * C * sizeof(E);
+    static constexpr size_t DOT = WKT + (size_t)DK * C * sizeof(E);
+    static constexpr size_t DUL = DOT + (size_t)DK * C * sizeof(E);
+    static constexpr size_t G = DUL + (size_t)C * DK * sizeof(E);
+    static constexpr size_t BYTES = ((G + (size_t)DK * sizeof(float)) + 255) / 256 * 256;
+};
 
-    __shared__ float colred[3][RG][DV];   // partial column sums: p, o, du
-    __shared__ float dotred[2][RG];       // partial kh . dkh, qh . dqh
+// Workspace of one backward call, in this order, each region 256-byte aligned.
+struct BwdLayout {
+    size_t cards, bcards, out, states, dstates, total;
+    __host__ __device__ BwdLayout(bool bf16, int64_t B, int64_t T, int H, int dk) {
+        const int64_t NC = (T + kChunk - 1) / kChunk;
+        const size_t chunks = (size_t)B * H * NC;
+        const size_t esz = bf16 ? 2 : 4;
+        const size_t card = bf16 ? (dk == 128 ? Card<__bf16, 128>::BYTES : Card<__bf16, 64>::BYTES)
+                                 : (dk == 128 ? Card<float, 128>::BYTES : Card<float, 64>::BYTES);
+        const size_t bcard = bf16 ? (dk == 128 ? BCard<__bf16, 128>::BYTES : BCard<__bf16, 64>::BYTES)
+                                  : (dk == 128 ? BCard<float, 128>::BYTES : BCard<float, 64>::BYTES);
+        cards = 0;
+        bcards = cards + up(chunks * card);
+        out = bcards + up(chunks * bcard);
+        states = out + up((size_t)B * T * H * dk * esz);
+        dstates = states + up(chunks * (size_t)dk * dk * 4);
+        total = dstates + up(chunks * (size_t)dk * dk * 4);
+    }
+    __host__ __device__ static size_t up(size_t x) { return (x + 255) / 256 * 256; }
+};
 
-    const int t = threadIdx.x, lane = t & 63, cg = t % CG, rg = t / CG;
-    const int64_t bh = blockIdx.x;
-    const int64_t b = bh / a.H;
-    const int h = (int)(bh % a.H);
+// one element of a lane fragment
+__device__ __forceinline__ float frag_elem(float v, int) { return v; }
+__device__ __forceinline__ float frag_elem(bf16x8 v, int e) { return (float)v[e]; }
+
+// Visit an R x K matrix stored in A-fragment order: f(row, k, value) for
+// every element, each lane fragment read with one load.
+template <typename E, int R, int K, typename F>
+__device__ __forceinline__ void for_each_frag(const char* src, int t, F f) {
+    constexpr int KF = MM<E>::KF, KS = MM<E>::KS;
+    typedef typename MM<E>::frag Fr;
+    for (int idx = t; idx < R * K / KF; idx += kThreads) {
+        const int blk = idx >> 6, lane = idx & 63;
+        const int row = 16 * (blk / (K / KS)) + (lane & 15);
+        const int k = (blk % (K / KS)) * KS + (lane >> 4) * KF;
+        const Fr v = reinterpret_cast<const Fr*>(src)[idx];
+#pragma unroll
+        for (int e = 0; e < KF; ++e) f(row, k + e, frag_elem(v, e));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. operands of the reverse hand-off (one workgroup per chunk-head)
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void kda_bwd_card_kernel(BackwardArgs a) {
+    using M = MM<E>;
+    using CL = Card<E, DK>;
+    using BC = BCard<E, DK>;
+    constexpr int C = kChunk, KS = M::KS, DV = DK;
+    constexpr int PAD = 16 / (int)sizeof(E);
+    constexpr int LDC = C + PAD;    // rows of C elements
+    constexpr int LDD = DK + PAD;   // rows of DK elements
+    constexpr int STAGE = DK * LDC > C * LDD ? DK * LDC : C * LDD;
+    __shared__ __attribute__((aligned(16))) E sStage[STAGE];
+    __shared__ __attribute__((aligned(16))) E sPT[C * LDC];    // P^T, row-major
+    __shared__ __attribute__((aligned(16))) E sDOT[DV * LDC];  // dO^T, row-major
+
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int H = a.H, NC = a.NC;
     const int64_t T = a.T;
-    const int NC = (int)((T + C - 1) / C);
-    const size_t SZ = (size_t)DK * DV;
-    // per (b, h): checkpoints [NC][DK][DV], then the chunk's entering states [C][DK][DV]
-    // (no workspace, and no use of it, when T == 0)
-    float* ckpt = a.ws + (T > 0 ? (size_t)bh * ((size_t)NC + C) * SZ : 0);
-    float* hist = ckpt + (size_t)NC * SZ;                        // [C][DK][DV]
-    const size_t blk = (size_t)(rg * RPT) * DV + 4 * cg;        // this thread's block origin
+    const int64_t wg = blockIdx.x;
+    const int h = (int)(wg % H);
+    const int64_t rest = wg / H;
+    const int c = (int)(rest % NC);
+    const int64_t b = rest / NC;
+    const int64_t bh = b * H + h;
+    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK);
+    const char* card = a.ws + L.cards + ((size_t)bh * NC + c) * CL::BYTES;
+    char* bcard = a.ws + L.bcards + ((size_t)bh * NC + c) * BC::BYTES;
+    const int64_t tok0 = (int64_t)c * C;
+    const int nvalid = (int)(T - tok0 < C ? T - tok0 : C);
 
-    auto row_of = [&](int64_t tok) { return ((size_t)b * T + tok) * a.H + h; };
+    // Ke (from Ke^T) -> row-major -> fragment order
+    for_each_frag<E, DK, C>(card + CL::KET, t, [&](int r, int k, float x) { sStage[k * LDD + r] = from_f32<E>(x); });
+    __syncthreads();
+    store_frag_order<E, C, DK>(bcard + BC::KEA, sStage, LDD, t);
+    __syncthreads();
+    // Qt^T
+    for_each_frag<E, C, DK>(card + CL::QT, t, [&](int r, int k, float x) { sStage[k * LDC + r] = from_f32<E>(x); });
+    __syncthreads();
+    store_frag_order<E, DK, C>(bcard + BC::QTT, sStage, LDC, t);
+    __syncthreads();
+    // -Wk^T
+    for_each_frag<E, C, DK>(card + CL::WK, t, [&](int r, int k, float x) { sStage[k * LDC + r] = from_f32<E>(-x); });
+    // P^T, and dO = d_out * sigmoid(g) transposed (zero on padded tokens)
+    for_each_frag<E, C, C>(card + CL::P, t, [&](int r, int k, float x) { sPT[k * LDC + r] = from_f32<E>(x); });
+    {
+        const size_t row0 = ((size_t)b * T + tok0) * H + h;
+        const E* dop = reinterpret_cast<const E*>(a.d_out);
+        const E* gp = reinterpret_cast<const E*>(a.g);
+        for (int idx = t; idx < C * DV / 4; idx += kThreads) {
+            const int i = idx / (DV / 4), v4 = (idx % (DV / 4)) * 4;
+            const size_t r = (row0 + (size_t)(i < nvalid ? i : nvalid - 1) * H) * DV + v4;
+            const f32x4 dy = dop ? ld4(dop + r) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 gg = ld4(gp + r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sDOT[(v4 + e) * LDC + i] = from_f32<E>(i < nvalid ? dy[e] * sigmoidf_(gg[e]) : 0.f);
+        }
+    }
+    if (t < DK) reinterpret_cast<float*>(bcard + BC::G)[t] = reinterpret_cast<const float*>(card + CL::GC)[t];
+    __syncthreads();
+    store_frag_order<E, DK, C>(bcard + BC::WKT, sStage, LDC, t);
+    store_frag_order<E, DV, C>(bcard + BC::DOT, sDOT, LDC, t);
+    // P^T dO: wave w takes column tiles [w*NT/4, (w+1)*NT/4), all token tiles
+    constexpr int NT = DV / 16, NTW = NT / 4;
+#pragma unroll
+    for (int jt = 0; jt < NTW; ++jt) {
+        const int ni = w * NTW + jt;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < C / KS; ++s)
+                x = M::mma(ld_frag(sPT, LDC, 16 * mi + n, s * KS, g), ld_frag(sDOT, LDC, 16 * ni + n, s * KS, g), x);
+            st4(reinterpret_cast<E*>(bcard + BC::DUL) + ((size_t)(ni * 4 + mi) * 64 + lane) * 4, x);
+        }
+    }
+}
 
-    // column sum over all rows of this thread's partial x (4 columns)
-    auto colsum = [&](int slot, f32x4 x) {
-        *reinterpret_cast<f32x4*>(&colred[slot][rg][4 * cg]) = x;
+// ---------------------------------------------------------------------------
+// 4. reverse hand-off: one workgroup per (batch row, head, 16-column slice),
+// chunks in reverse.  Wave w owns dU rows (tokens) 16w..16w+15 and dS rows
+// w*DK/4 .. (w+1)*DK/4 - 1; dS^T and dU^T cross waves through LDS.
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) {
+    using M = MM<E>;
+    using BC = BCard<E, DK>;
+    typedef typename M::frag F;
+    constexpr int C = kChunk, KS = M::KS, KF = M::KF, DV = DK;
+    constexpr int NT = DV / 16, MTS = DK / 64, NKD = DK / KS, NKC = C / KS;
+    constexpr int PADE = 16 / (int)sizeof(E);
+    constexpr int LDS_S = DK + PADE, LDS_U = C + PADE;
+    constexpr uint32_t FB = KF * sizeof(E), KSB = 64 * FB;
+    __shared__ __attribute__((aligned(16))) E sS[16 * LDS_S];
+    __shared__ __attribute__((aligned(16))) E sU[16 * LDS_U];
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4, n = lane & 15;
+    const int NC = a.NC;
+    const int64_t BH = a.B * (int64_t)a.H;
+    const int64_t x = blockIdx.x;
+    const int xcd = (int)(x % kXcds);
+    const int64_t slot = x / kXcds;
+    const int tile = (int)(slot % NT);
+    const int64_t bh = (slot / NT) * kXcds + xcd;
+    if (bh >= BH) return;
+    const int col0 = 16 * tile;
+    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK);
+
+    f32x4 dS[MTS];
+#pragma unroll
+    for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = (DK / 4) * w + 16 * mt + 4 * g + e;
+            dS[mt][e] = a.d_state ? a.d_state[((size_t)bh * DK + r) * DV + col0 + n] : 0.f;
+        }
+#pragma unroll
+    for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, dS[mt]);
+    __syncthreads();
+
+    const char* bcards = a.ws + L.bcards + (size_t)bh * NC * BC::BYTES;
+    float* dstates = reinterpret_cast<float*>(a.ws + L.dstates) + (size_t)bh * NC * DK * DV + col0 + n;
+    for (int c = NC - 1; c >= 0; --c) {
+        const char* bc = bcards + (size_t)c * BC::BYTES;
+        float* dst = dstates + (size_t)c * DK * DV;   // gradient of the state leaving chunk c
+#pragma unroll
+        for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(size_t)((DK / 4) * w + 16 * mt + 4 * g + e) * DV] = dS[mt][e];
+        // dU rows 16w..16w+15 = P^T dO + Ke dS
+        f32x4 du = ld4(reinterpret_cast<const E*>(bc + BC::DUL) + ((size_t)(tile * 4 + w) * 64 + lane) * 4);
+#pragma unroll
+        for (int s = 0; s < NKD; ++s)
+            du = M::mma(*reinterpret_cast<const F*>(bc + BC::KEA + (w * NKD + s) * KSB + lane * FB),
+                        ld_frag(sS, LDS_S, n, s * KS, g), du);
+        st4(sU + n * LDS_U + 16 * w + 4 * g, du);
         __syncthreads();
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        // dS <- G dS + Qt^T dO - Wk^T dU
+        F ub[NKC], ob[NKC];
 #pragma unroll
-        for (int j = 0; j < RG; ++j) s += *reinterpret_cast<const f32x4*>(&colred[slot][j][4 * cg]);
-        return s;
-    };
-    // row sum over the CG column groups (lanes of one wave)
-    auto rowsum = [&](float x) {
+        for (int s = 0; s < NKC; ++s) {
+            ub[s] = ld_frag(sU, LDS_U, n, s * KS, g);
+            ob[s] = *reinterpret_cast<const F*>(bc + BC::DOT + (tile * NKC + s) * KSB + lane * FB);
+        }
 #pragma unroll
-        for (int m = 1; m < CG; m <<= 1) x += __shfl_xor(x, m);
-        return x;
-    };
-    // per-token row data: normalised k and q on this thread's rows, the
-    // decays, and the norms (each wave sweeps the full vectors)
-    struct Tok {
-        float kh[RPT], qh[RPT], D[RPT], la[RPT];
-        float nk, nq, beta;
-        f32x4 v;
-    };
-    auto load_tok = [&](int64_t tok, Tok& x) {
-        const size_t row = row_of(tok);
-        const E* k = reinterpret_cast<const E*>(a.k) + row * DK;
-        const E* q = reinterpret_cast<const E*>(a.q) + row * DK;
+        for (int mt = 0; mt < MTS; ++mt) {
+            const int rb = (DK / 64) * w + mt;
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(bc + BC::G + ((DK / 4) * w + 16 * mt + 4 * g) * 4);
+            f32x4 acc = dS[mt] * gv;
+#pragma unroll
+            for (int s = 0; s < NKC; ++s)
+                acc = M::mma(*reinterpret_cast<const F*>(bc + BC::QTT + (rb * NKC + s) * KSB + lane * FB), ob[s], acc);
+#pragma unroll
+            for (int s = 0; s < NKC; ++s)
+                acc = M::mma(*reinterpret_cast<const F*>(bc + BC::WKT + (rb * NKC + s) * KSB + lane * FB), ub[s], acc);
+            dS[mt] = acc;
+        }
+#pragma unroll
+        for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, dS[mt]);
+        __syncthreads();
+    }
+    if (a.d_state_in) {
+#pragma unroll
+        for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = (DK / 4) * w + 16 * mt + 4 * g + e;
+                a.d_state_in[((size_t)bh * DK + r) * DV + col0 + n] = dS[mt][e];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 5. token gradients: one workgroup per chunk-head, fp32 throughout (LDS and
+// fp32 MFMA).  The value-side quantities (R, U, dO, dU) go through in
+// 16-column blocks; the products that contract over the value columns
+// accumulate in registers across the blocks.
+template <int DK>
+struct GradLds {
+    static constexpr int C = kChunk, NB = 16;
+    static constexpr int LDK = DK + 4;   // [C][DK] rows
+    static constexpr int LDC = C + 4;    // [C][C] rows
+    static constexpr int LDB = NB + 4;   // [C][NB] rows
+    static constexpr size_t K = 0;                          // k^ (zero on padded tokens)
+    static constexpr size_t Q = K + (size_t)C * LDK * 4;    // q^
+    static constexpr size_t EG = Q + (size_t)C * LDK * 4;   // e^gamma
+    static constexpr size_t P = EG + (size_t)C * LDK * 4;   // P, then dP, then dgamma (spans P and T)
+    static constexpr size_t T = P + (size_t)C * LDC * 4;    // diag(beta) A -> T, then dA
+    static constexpr size_t R = T + (size_t)C * LDC * 4;
+    static constexpr size_t U = R + (size_t)C * LDB * 4;
+    static constexpr size_t DO = U + (size_t)C * LDB * 4;
+    static constexpr size_t DU = DO + (size_t)C * LDB * 4;  // dU, then dU~
+    static constexpr size_t BETA = DU + (size_t)C * LDB * 4;
+    static constexpr size_t NK = BETA + (size_t)C * 4;      // |k|
+    static constexpr size_t NQ = NK + (size_t)C * 4;        // |q|
+    static constexpr size_t DGC = NQ + (size_t)C * 4;       // [5][DK]: per-wave sum dKe*Ke, rowsum(S0*dS)
+    static constexpr size_t BYTES = DGC + (size_t)5 * DK * 4;
+    static_assert((size_t)C * LDK <= 2 * (size_t)C * LDC, "dgamma fits over P and T");
+};
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs a) {
+    using LY = GradLds<DK>;
+    constexpr int C = kChunk, NB = LY::NB, DV = DK;
+    constexpr int LDK = LY::LDK, LDC = LY::LDC, LDB = LY::LDB;
+    constexpr int NT = DK / 16;   // channel tiles
+    constexpr int NKD = DK / 4;   // fp32 MFMA k-steps over the channels
+    constexpr int NKC = C / 4;    // ... over the tokens
+    constexpr float kLog2e = 1.4426950408889634f;
+
+    __shared__ __attribute__((aligned(16))) char lds[LY::BYTES];
+    float* sK = reinterpret_cast<float*>(lds + LY::K);
+    float* sQ = reinterpret_cast<float*>(lds + LY::Q);
+    float* sEG = reinterpret_cast<float*>(lds + LY::EG);
+    float* sP = reinterpret_cast<float*>(lds + LY::P);
+    float* sT = reinterpret_cast<float*>(lds + LY::T);
+    float* sR = reinterpret_cast<float*>(lds + LY::R);
+    float* sU = reinterpret_cast<float*>(lds + LY::U);
+    float* sDO = reinterpret_cast<float*>(lds + LY::DO);
+    float* sDU = reinterpret_cast<float*>(lds + LY::DU);
+    float* sBeta = reinterpret_cast<float*>(lds + LY::BETA);
+    float* sNk = reinterpret_cast<float*>(lds + LY::NK);
+    float* sNq = reinterpret_cast<float*>(lds + LY::NQ);
+    float* sDGC = reinterpret_cast<float*>(lds + LY::DGC);
+    float* sDG = sP;
+
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int H = a.H, NC = a.NC;
+    const int64_t T = a.T;
+    const int64_t wg = blockIdx.x;
+    const int h = (int)(wg % H);
+    const int64_t rest = wg / H;
+    const int c = (int)(rest % NC);
+    const int64_t b = rest / NC;
+    const int64_t bh = b * H + h;
+    const int64_t tok0 = (int64_t)c * C;
+    const int nvalid = (int)(T - tok0 < C ? T - tok0 : C);
+    const size_t row0 = ((size_t)b * T + tok0) * H + h;
+    // token row of chunk token i (padded tokens re-read the last valid row)
+    auto rowi = [&](int i) { return row0 + (size_t)(i < nvalid ? i : nvalid - 1) * H; };
+    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK);
+    const float* S0 = reinterpret_cast<const float*>(a.ws + L.states) + ((size_t)bh * NC + c) * DK * DV;
+    const float* dSo = reinterpret_cast<const float*>(a.ws + L.dstates) + ((size_t)bh * NC + c) * DK * DV;
+    const E* qp = reinterpret_cast<const E*>(a.q);
+    const E* kp = reinterpret_cast<const E*>(a.k);
+
+    // ---- 1: norms, k^, q^, e^gamma, beta ----
+    for (int ii = 0; ii < 16; ++ii) {
+        const int i = 16 * w + ii;
+        const size_t r = rowi(i);
         float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const float kk = to_f32(k[lane * EPL + e]), qq = to_f32(q[lane * EPL + e]);
-            sk += kk * kk; sq += qq * qq;
+        for (int e = 0; e < DK / 64; ++e) {
+            const float kk = to_f32(kp[r * DK + lane * (DK / 64) + e]), qq = to_f32(qp[r * DK + lane * (DK / 64) + e]);
+            sk += kk * kk;
+            sq += qq * qq;
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             sk += __shfl_xor(sk, off);
             sq += __shfl_xor(sq, off);
         }
-        x.nk = sqrtf(sk);
-        x.nq = sqrtf(sq);
-        const float rk = 1.0f / fmaxf(x.nk, 1e-6f), rq = 1.0f / fmaxf(x.nq, 1e-6f);
-        const float* la = a.log_alpha + row * DK;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg * RPT + i;
-            x.kh[i] = to_f32(k[r]) * rk;
-            x.qh[i] = to_f32(q[r]) * rq;
-            x.la[i] = la[r];
-            x.D[i] = __expf(fmaxf(la[r], a.floor_));
+        if (lane == 0) {
+            sNk[i] = sqrtf(sk);
+            sNq[i] = sqrtf(sq);
         }
-        x.beta = a.beta[row];
-        x.v = ld4(reinterpret_cast<const E*>(a.v) + row * DV + 4 * cg);
-    };
-
-    f32x4 S[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        S[i] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + bh * SZ + blk + (size_t)i * DV)
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // one forward step on S (retention, prediction, corrective write)
-    auto fwd = [&](const Tok& x) {
-        f32x4 pp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            S[i] = S[i] * x.D[i];
-            pp += S[i] * x.kh[i];
-        }
-        const f32x4 p = colsum(0, pp);
-        const f32x4 u = x.beta * (x.v - p);
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) S[i] += x.kh[i] * u;
-        __syncthreads();   // colred[0] is reused by the next step
-    };
-
-    // ---- phase 1: checkpoints ----
-    for (int64_t tok = 0; tok < T; ++tok) {
-        if (tok % C == 0) {
-#pragma unroll
-            for (int i = 0; i < RPT; ++i)
-                *reinterpret_cast<f32x4*>(ckpt + (size_t)(tok / C) * SZ + blk + (size_t)i * DV) = S[i];
-        }
-        Tok x;
-        load_tok(tok, x);
-        fwd(x);
     }
+    if (t < C) sBeta[t] = t < nvalid ? a.beta[rowi(t)] : 0.f;
+    for (int idx = t; idx < C * LDC; idx += kThreads) sT[idx] = 0.f;   // T's upper tiles stay zero
+    __syncthreads();
+    for (int idx = t; idx < C * DK; idx += kThreads) {
+        const int i = idx / DK, ch = idx % DK;
+        const size_t r = rowi(i);
+        const bool ok = i < nvalid;
+        sK[i * LDK + ch] = ok ? to_f32(kp[r * DK + ch]) / fmaxf(sNk[i], 1e-6f) : 0.f;
+        sQ[i * LDK + ch] = ok ? to_f32(qp[r * DK + ch]) / fmaxf(sNq[i], 1e-6f) : 0.f;
+    }
+    if (t < DK) {   // cumulative log-decay of channel t (base 2), padded tokens add nothing
+        float run = 0.f;
+        for (int i = 0; i < C; ++i) {
+            const float la = a.log_alpha[rowi(i) * DK + t];
+            run += i < nvalid ? fmaxf(la, a.floor_) * kLog2e : 0.f;
+            sEG[i * LDK + t] = __builtin_amdgcn_exp2f(run);
+        }
+    }
+    __syncthreads();
 
-    // ---- phase 2: chunks in reverse ----
-    f32x4 dS[RPT];
+    auto Kt = [&](int i, int ch) { return sK[i * LDK + ch] * sEG[i * LDK + ch]; };
+    auto Kh = [&](int i, int ch) { return sK[i * LDK + ch] * __builtin_amdgcn_rcpf(sEG[i * LDK + ch]); };
+    auto Qt = [&](int i, int ch) { return sQ[i * LDK + ch] * sEG[i * LDK + ch]; };
+    auto Ke = [&](int i, int ch) { return Kh(i, ch) * sEG[(C - 1) * LDK + ch]; };
+
+    // ---- 2: diag(beta) A -> sT (strictly lower), P -> sP ----
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        dS[i] = a.d_state ? *reinterpret_cast<const f32x4*>(a.d_state + bh * SZ + blk + (size_t)i * DV)
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c = NC - 1; c >= 0; --c) {
-        const int64_t t0 = (int64_t)c * C;
-        const int n = (int)(T - t0 < C ? T - t0 : C);
-        // recompute the entering states of the chunk's tokens
+    for (int j = 0; j < 4; ++j) {
+        if (j <= w) {
+            f32x4 xa = {0.f, 0.f, 0.f, 0.f}, xp = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < NKD; ++s) {
+                const float kh = Kh(16 * j + n, 4 * s + g);
+                xa = mma_f32(Kt(16 * w + n, 4 * s + g), kh, xa);
+                xp = mma_f32(Qt(16 * w + n, 4 * s + g), kh, xp);
+            }
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) S[i] = *reinterpret_cast<const f32x4*>(ckpt + (size_t)c * SZ + blk + (size_t)i * DV);
-        for (int j = 0; j < n; ++j) {
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w + 4 * g + e, jj = 16 * j + n;
+                sT[i * LDC + jj] = jj < i ? sBeta[i] * xa[e] : 0.f;
+                sP[i * LDC + jj] = jj <= i ? xp[e] : 0.f;
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) *reinterpret_cast<f32x4*>(hist + (size_t)j * SZ + blk + (size_t)i * DV) = S[i];
-            if (j + 1 < n) {
-                Tok x;
-                load_tok(t0 + j, x);
-                fwd(x);
+            for (int e = 0; e < 4; ++e) sP[(16 * w + 4 * g + e) * LDC + 16 * j + n] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3: T = (I + diag(beta) A)^-1 in place (blocked substitution) ----
+    {   // diagonal 16x16 blocks by forward substitution; lane n of wave w owns column n of block w
+        float x[16];
+        if (g == 0) {
+            const float* Ab = sT + (16 * w) * LDC + 16 * w;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == n) ? 1.f : 0.f;
+#pragma unroll
+                for (int kk = 0; kk < i; ++kk) s -= Ab[i * LDC + kk] * x[kk];
+                x[i] = s;
             }
         }
         __syncthreads();
-        // tokens in reverse
-        for (int j = n - 1; j >= 0; --j) {
-            const int64_t tok = t0 + j;
-            const size_t row = row_of(tok);
-            Tok x;
-            load_tok(tok, x);
-            f32x4 Sp[RPT];
-            f32x4 pp = {0.f, 0.f, 0.f, 0.f};
+        if (g == 0) {
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                Sp[i] = *reinterpret_cast<const f32x4*>(hist + (size_t)j * SZ + blk + (size_t)i * DV) * x.D[i];
-                pp += Sp[i] * x.kh[i];
+            for (int i = 0; i < 16; ++i) sT[(16 * w + i) * LDC + 16 * w + n] = x[i];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {   // block row i: T_ij = -D_i sum_{kb=j}^{i-1} A_{i,kb} T_{kb,j}, wave j
+        f32x4 tij = {0.f, 0.f, 0.f, 0.f};
+        if (w < i) {
+            const int j = w;
+            f32x4 xx = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = j; kb < i; ++kb) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    xx = mma_f32(sT[(16 * i + n) * LDC + 16 * kb + 4 * s + g], sT[(16 * kb + 4 * s + g) * LDC + 16 * j + n],
+                                 xx);
             }
-            const f32x4 p = colsum(0, pp);
-            const f32x4 u = x.beta * (x.v - p);
-            f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+            // D_i X with X straight from the accumulator: at step s lane group g
+            // holds X[4g + s][n], so A supplies D_i[m][4g + s]
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) oo += (Sp[i] + x.kh[i] * u) * x.qh[i];
-            const f32x4 o = colsum(1, oo);
-            // output gate
-            const f32x4 dy = a.d_out ? ld4(reinterpret_cast<const E*>(a.d_out) + row * DV + 4 * cg)
-                                     : f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 gg = ld4(reinterpret_cast<const E*>(a.g) + row * DV + 4 * cg);
-            f32x4 dov, dgv;
+            for (int s = 0; s < 4; ++s) tij = mma_f32(sT[(16 * i + n) * LDC + 16 * i + 4 * g + s], xx[s], tij);
+        }
+        __syncthreads();
+        if (w < i) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float sg = sigmoidf_(gg[e]);
-                dov[e] = dy[e] * sg;
-                dgv[e] = dy[e] * o[e] * sg * (1.f - sg);
-            }
-            if (rg == 0) st4(reinterpret_cast<E*>(a.dg) + row * DV + 4 * cg, dgv);
-            // dqh = S do (S after the write), dS += qh do^T, du = dS^T kh
-            float dqh[RPT];
-            f32x4 dd = {0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * g + e) * LDC + 16 * w + n] = -tij[e];
+        }
+        __syncthreads();
+    }
+
+    // ---- 4: value columns in blocks of NB ----
+    const E* vp = reinterpret_cast<const E*>(a.v);
+    const E* gp = reinterpret_cast<const E*>(a.g);
+    const E* op = reinterpret_cast<const E*>(a.ws + L.out);
+    const E* dop = reinterpret_cast<const E*>(a.d_out);
+    E* dvp = reinterpret_cast<E*>(a.dv);
+    E* dgp = reinterpret_cast<E*>(a.dg);
+    f32x4 dQt[NT], dKt[NT], dKe[NT], dMa[4], dPa[4];
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const f32x4 St = Sp[i] + x.kh[i] * u;
-                dqh[i] = rowsum(St[0] * dov[0] + St[1] * dov[1] + St[2] * dov[2] + St[3] * dov[3]);
-                dS[i] += x.qh[i] * dov;
-                dd += dS[i] * x.kh[i];
-            }
-            const f32x4 du = colsum(2, dd);
-            if (rg == 0) {
-                st4(reinterpret_cast<E*>(a.dv) + row * DV + 4 * cg, x.beta * du);
-                const f32x4 vp = x.v - p;
-                const float db = rowsum(du[0] * vp[0] + du[1] * vp[1] + du[2] * vp[2] + du[3] * vp[3]);
-                if (cg == 0) a.dbeta[row] = db;
-            }
-            const f32x4 dp = -x.beta * du;
-            // dkh = dS u + S' dp; dS' = dS + kh dp^T; dlambda; dS_prev = D dS'
-            float dkh[RPT];
-            float kdot = 0.f, qdot = 0.f;
+    for (int ct = 0; ct < NT; ++ct) dQt[ct] = dKt[ct] = dKe[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const f32x4 m = dS[i] * u + Sp[i] * dp;
-                dkh[i] = rowsum(m[0] + m[1] + m[2] + m[3]);
-                dS[i] += x.kh[i] * dp;
-                const f32x4 l = Sp[i] * dS[i];
-                const float dl = rowsum(l[0] + l[1] + l[2] + l[3]);
-                if (cg == i)   // one lane per row writes
-                    a.dlog_alpha[row * DK + rg * RPT + i] = x.la[i] > a.floor_ ? dl : 0.f;
-                dS[i] *= x.D[i];
-                kdot += x.kh[i] * dkh[i];
-                qdot += x.qh[i] * dqh[i];
-            }
-            // L2 normalisation: dx = (dxh - xh (xh . dxh)) / |x| (constant divisor below 1e-6)
-            if (cg == 0) {
-                dotred[0][rg] = kdot;
-                dotred[1][rg] = qdot;
-            }
-            __syncthreads();
-            float kd = 0.f, qd = 0.f;
+    for (int j = 0; j < 4; ++j) dMa[j] = dPa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 dbp = {0.f, 0.f, 0.f, 0.f};
+    for (int vb = 0; vb < DV / NB; ++vb) {
+        const int col0 = NB * vb;
+        // R = V - Kt S0 (rows 16w.., this block's columns)
+        f32x4 r;
 #pragma unroll
-            for (int r = 0; r < RG; ++r) { kd += dotred[0][r]; qd += dotred[1][r]; }
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * g + e;
+            r[e] = i < nvalid ? to_f32(vp[rowi(i) * DV + col0 + n]) : 0.f;
+        }
+        for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w + n, 4 * s + g), S0[(size_t)(4 * s + g) * DV + col0 + n], r);
+        // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g))
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                if (cg == i) {
-                    const int r = rg * RPT + i;
-                    reinterpret_cast<E*>(a.dk)[row * DK + r] =
-                        from_f32<E>(x.nk < 1e-6f ? dkh[i] * 1e6f : (dkh[i] - x.kh[i] * kd) / x.nk);
-                    reinterpret_cast<E*>(a.dq)[row * DK + r] =
-                        from_f32<E>(x.nq < 1e-6f ? dqh[i] * 1e6f : (dqh[i] - x.qh[i] * qd) / x.nq);
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * g + e;
+            const size_t ri = rowi(i) * DV + col0 + n;
+            const float dy = dop ? to_f32(dop[ri]) : 0.f;
+            const float sg = sigmoidf_(to_f32(gp[ri]));
+            sR[i * LDB + n] = r[e];
+            sDO[i * LDB + n] = i < nvalid ? dy * sg : 0.f;
+            if (i < nvalid) dgp[ri] = from_f32<E>(dy * to_f32(op[ri]) * (1.f - sg));
+        }
+        __syncthreads();
+        // U = T diag(beta) R (T lower triangular)
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4 * (w + 1); ++s)
+            u = mma_f32(sT[(16 * w + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sU[(16 * w + 4 * g + e) * LDB + n] = u[e];
+        // dU = Ke dS + P^T dO (P^T upper triangular)
+        f32x4 du = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w + n, 4 * s + g), dSo[(size_t)(4 * s + g) * DV + col0 + n], du);
+        for (int s = 4 * w; s < NKC; ++s) du = mma_f32(sP[(4 * s + g) * LDC + 16 * w + n], sDO[(4 * s + g) * LDB + n], du);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDU[(16 * w + 4 * g + e) * LDB + n] = du[e];
+        __syncthreads();
+        // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
+        f32x4 dut = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 4 * w; s < NKC; ++s) dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w + n], sDU[(4 * s + g) * LDB + n], dut);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * g + e;
+            if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
+            dbp[e] += dut[e] * sR[i * LDB + n];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDU[(16 * w + 4 * g + e) * LDB + n] = dut[e];
+        __syncthreads();
+        // dM -= dU~ U^T, dP += dO U^T (column tiles j <= w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j <= w) {
+#pragma unroll
+                for (int s = 0; s < NB / 4; ++s) {
+                    const float ub = sU[(16 * j + n) * LDB + 4 * s + g];
+                    dMa[j] = mma_f32(-sDU[(16 * w + n) * LDB + 4 * s + g], ub, dMa[j]);
+                    dPa[j] = mma_f32(sDO[(16 * w + n) * LDB + 4 * s + g], ub, dPa[j]);
                 }
             }
-            __syncthreads();   // colred and dotred are reused by the next token
+        }
+        // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T
+#pragma unroll
+        for (int s = 0; s < NB / 4; ++s) {
+            const float ao = sDO[(16 * w + n) * LDB + 4 * s + g];
+            const float ar = -sBeta[16 * w + n] * sDU[(16 * w + n) * LDB + 4 * s + g];
+            const float au = sU[(16 * w + n) * LDB + 4 * s + g];
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const size_t si = (size_t)(16 * ct + n) * DV + col0 + 4 * s + g;
+                const float b0 = S0[si], b1 = dSo[si];
+                dQt[ct] = mma_f32(ao, b0, dQt[ct]);
+                dKt[ct] = mma_f32(ar, b0, dKt[ct]);
+                dKe[ct] = mma_f32(au, b1, dKe[ct]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- 5: dbeta; dA and dP to LDS ----
+    {
+        f32x4 db = dbp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j <= w) {   // A tile (w, j) again, for sum_j dM_ij A_ij
+                f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < NKD; ++s) xa = mma_f32(Kt(16 * w + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), xa);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * j + n < 16 * w + 4 * g + e) db[e] += dMa[j][e] * xa[e];
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) db[e] += __shfl_xor(db[e], m);
+        if (n == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w + 4 * g + e;
+                if (i < nvalid) a.dbeta[rowi(i)] = db[e];
+            }
         }
     }
-    if (a.d_state_in) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) *reinterpret_cast<f32x4*>(a.d_state_in + bh * SZ + blk + (size_t)i * DV) = dS[i];
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * g + e, jj = 16 * j + n;
+            sT[i * LDC + jj] = (j <= w && jj < i) ? sBeta[i] * dMa[j][e] : 0.f;   // dA
+            sP[i * LDC + jj] = (j <= w && jj <= i) ? dPa[j][e] : 0.f;            // dP
+        }
+    __syncthreads();
+
+    // ---- 6: dQt += dP Kh, dKt += dA Kh, dKh = dP^T Qt + dA^T Kt ----
+    f32x4 dKh[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) dKh[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4 * (w + 1); ++s) {
+        const float ap = sP[(16 * w + n) * LDC + 4 * s + g], aa = sT[(16 * w + n) * LDC + 4 * s + g];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const float kh = Kh(4 * s + g, 16 * ct + n);
+            dQt[ct] = mma_f32(ap, kh, dQt[ct]);
+            dKt[ct] = mma_f32(aa, kh, dKt[ct]);
+        }
+    }
+    for (int s = 4 * w; s < NKC; ++s) {
+        const float ap = sP[(4 * s + g) * LDC + 16 * w + n], aa = sT[(4 * s + g) * LDC + 16 * w + n];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            dKh[ct] = mma_f32(ap, Qt(4 * s + g, 16 * ct + n), dKh[ct]);
+            dKh[ct] = mma_f32(aa, Kt(4 * s + g, 16 * ct + n), dKh[ct]);
+        }
+    }
+
+    // ---- 7: through the decay folding: dq^, dk^, dgamma (in place) ----
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        const int ch = 16 * ct + n;
+        const float egc = sEG[(C - 1) * LDK + ch];
+        float gsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * g + e;
+            const float kh = sK[i * LDK + ch], qh = sQ[i * LDK + ch], eg = sEG[i * LDK + ch];
+            const float ieg = __builtin_amdgcn_rcpf(eg);
+            const float ktv = kh * eg, khv = kh * ieg, qtv = qh * eg, kev = khv * egc;
+            const float dqt = dQt[ct][e], dkt = dKt[ct][e], dkhv = dKh[ct][e], dke = dKe[ct][e];
+            dQt[ct][e] = dqt * eg;                                          // dq^
+            dKt[ct][e] = dkt * eg + dkhv * ieg + dke * egc * ieg;           // dk^
+            dKh[ct][e] = dkt * ktv - dkhv * khv + dqt * qtv - dke * kev;    // dgamma
+            gsum += dke * kev;
+        }
+        gsum += __shfl_xor(gsum, 16);
+        gsum += __shfl_xor(gsum, 32);
+        if (g == 0) sDGC[w * DK + ch] = gsum;
+    }
+    // ---- 8: L2 normalisation: dx = (dx^ - x^ (x^ . dx^)) / |x| (constant divisor below 1e-6) ----
+    {
+        f32x4 kd = {0.f, 0.f, 0.f, 0.f}, qd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w + 4 * g + e, ch = 16 * ct + n;
+                kd[e] += sK[i * LDK + ch] * dKt[ct][e];
+                qd[e] += sQ[i * LDK + ch] * dQt[ct][e];
+            }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kd[e] += __shfl_xor(kd[e], m);
+                qd[e] += __shfl_xor(qd[e], m);
+            }
+        E* dkp = reinterpret_cast<E*>(a.dk);
+        E* dqp = reinterpret_cast<E*>(a.dq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * g + e;
+            if (i < nvalid) {
+                const float nk = sNk[i], nq = sNq[i];
+                const size_t ri = rowi(i) * DK;
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct) {
+                    const int ch = 16 * ct + n;
+                    const float dkx = nk < 1e-6f ? dKt[ct][e] * 1e6f : (dKt[ct][e] - sK[i * LDK + ch] * kd[e]) / nk;
+                    const float dqx = nq < 1e-6f ? dQt[ct][e] * 1e6f : (dQt[ct][e] - sQ[i * LDK + ch] * qd[e]) / nq;
+                    dkp[ri + ch] = from_f32<E>(dkx);
+                    dqp[ri + ch] = from_f32<E>(dqx);
+                }
+            }
+        }
+    }
+    // ---- 9: dgamma to LDS (over dP and dA), rowsum(S0 * dS) per key channel ----
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDG[(16 * w + 4 * g + e) * LDK + 16 * ct + n] = dKh[ct][e];
+    for (int ch = w; ch < DK; ch += 4) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < DV / 64; ++e) {
+            const size_t si = (size_t)ch * DV + lane * (DV / 64) + e;
+            s += S0[si] * dSo[si];
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off);
+        if (lane == 0) sDGC[4 * DK + ch] = s;
+    }
+    __syncthreads();
+    // ---- 10: dlog_alpha = reverse cumulative sum of dgamma (zero where the floor binds) ----
+    if (t < DK) {
+        const float egc = sEG[(C - 1) * LDK + t];
+        float acc = sDGC[t] + sDGC[DK + t] + sDGC[2 * DK + t] + sDGC[3 * DK + t] + egc * sDGC[4 * DK + t];
+        for (int i = nvalid - 1; i >= 0; --i) {
+            acc += sDG[i * LDK + t];
+            const size_t ri = rowi(i) * DK + t;
+            a.dlog_alpha[ri] = a.log_alpha[ri] > a.floor_ ? acc : 0.f;
+        }
     }
 }
 
 template <typename E, int DK>
 hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
-    const int64_t blocks = a.B * (int64_t)a.H;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((kda_backward_kernel<E, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    const int64_t BH = a.B * (int64_t)a.H;
+    if (BH == 0) return hipSuccess;
+    const int64_t chunks = BH * a.NC;
+    if (chunks > 0) {
+        hipLaunchKernelGGL((kda_bwd_card_kernel<E, DK>), dim3((unsigned)chunks), dim3(kThreads), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t groups = (BH + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((kda_bwd_scan_kernel<E, DK>), dim3((unsigned)(groups * kXcds * (DK / 16))), dim3(kThreads), 0, s,
+                       a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || chunks == 0) return e;
+    hipLaunchKernelGGL((kda_bwd_grad_kernel<E, DK>), dim3((unsigned)chunks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(int64_t B, int64_t T, int H, int dk) {
-    const int64_t NC = (T + kChunk - 1) / kChunk;
-    return T == 0 ? 0 : (size_t)B * H * (size_t)(NC + kChunk) * dk * dk * sizeof(float);
+size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk) {
+    return T == 0 ? 0 : BwdLayout(bf16, B, T, H, dk).total;
 }
 
 hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t s) {
+    const BwdLayout L(bf16, a.B, a.T, a.H, dk);
+    if (a.NC > 0 && a.B > 0) {   // forward cards, then the forward hand-off keeping every chunk's entering state
+        PrepareArgs p;
+        p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.beta = a.beta;
+        p.ws = a.ws + L.cards;
+        p.B = a.B; p.T = a.T; p.H = a.H; p.NC = a.NC; p.floor_ = a.floor_;
+        hipError_t e = launch_prepare(bf16, dk, p, s);
+        if (e != hipSuccess) return e;
+        ScanArgs f = {};
+        f.ws = a.ws + L.cards;
+        f.g = a.g; f.state_in = a.state_in; f.out = a.ws + L.out;
+        f.states = reinterpret_cast<float*>(a.ws + L.states);
+        f.B = a.B; f.T = a.T; f.H = a.H; f.NC = a.NC;
+        e = launch_scan(bf16, dk, false, f, s);
+        if (e != hipSuccess) return e;
+    }
     if (bf16) return dk == 128 ? launch_backward_t<__bf16, 128>(a, s) : launch_backward_t<__bf16, 64>(a, s);
     return dk == 128 ? launch_backward_t<float, 128>(a, s) : launch_backward_t<float, 64>(a, s);
 }

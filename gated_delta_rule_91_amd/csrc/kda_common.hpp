@@ -134,4 +134,27 @@ __host__ __device__ constexpr int frag_index(int row, int k, int K) {
             ((k % MM<E>::KS) / MM<E>::KF) * 16 + (row & 15)) * MM<E>::KF + (k % MM<E>::KF);
 }
 
+// Copy an R x K row-major LDS matrix (leading dimension ld) to global
+// memory in MFMA A-fragment order (the Card layout above).
+template <typename E, int R, int K>
+__device__ __forceinline__ void store_frag_order(char* dst, const E* src, int ld, int t) {
+    constexpr int KF = MM<E>::KF, KS = MM<E>::KS;
+    if constexpr (KF == 8) {   // a lane fragment is one 16-byte run of a source row
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        for (int idx = t; idx < R * K / 8; idx += kThreads) {
+            const int blk = idx >> 6, lane = idx & 63;
+            const int row = 16 * (blk / (K / KS)) + (lane & 15);
+            const int k = (blk % (K / KS)) * KS + (lane >> 4) * KF;
+            *reinterpret_cast<u32x4*>(dst + (size_t)idx * 16) = *reinterpret_cast<const u32x4*>(src + row * ld + k);
+        }
+    } else {
+        for (int idx = t; idx < R * K; idx += kThreads) {
+            const int blk = idx >> 6, lane = idx & 63;
+            const int row = 16 * (blk / (K / KS)) + (lane & 15);
+            const int k = (blk % (K / KS)) * KS + (lane >> 4);
+            reinterpret_cast<E*>(dst)[idx] = src[row * ld + k];
+        }
+    }
+}
+
 }  // namespace kda

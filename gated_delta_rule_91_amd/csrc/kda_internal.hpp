@@ -29,6 +29,7 @@ struct ScanArgs {
     float* state_out;        // [B,H,dk,dv] or null
     float* transition;       // summary mode: [B,H,dk,dk]
     float* zero_state;       // summary mode: [B,H,dk,dv]
+    float* states;           // or null; else the state entering every chunk, [B,H,NC,dk,dv]
     int64_t B, T;
     int H, NC;
 };
@@ -74,14 +75,14 @@ struct BackwardArgs {
     float* dbeta;            // [B,T,H]
     void* dg;                // [B,T,H,dv] io dtype
     float* d_state_in;       // [B,H,dk,dv] or null
-    float* ws;               // backward_workspace_bytes
+    char* ws;                // backward_workspace_bytes
     int64_t B, T;
-    int H;
+    int H, NC;
     float floor_;
 };
 
 size_t card_bytes(bool bf16, int dk);
-size_t backward_workspace_bytes(int64_t B, int64_t T, int H, int dk);
+size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk);
 hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t s);
 hipError_t launch_prepare(bool bf16, int dk, const PrepareArgs& a, hipStream_t s);
 hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s);

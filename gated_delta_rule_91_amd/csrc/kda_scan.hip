@@ -147,7 +147,7 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
 constexpr int kRing4 = 4;
 constexpr int kPrefetch = kRing4 + 1;
 
-template <typename E, int DK, int NTW, bool SUMMARY>
+template <typename E, int DK, int NTW, bool SUMMARY, bool CKPT>
 __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     using M = MM<E>;
     using CL = Card<E, DK>;
@@ -237,6 +237,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     auto step = [&](auto full, const O& cur, int c) {
         constexpr bool FULL = decltype(full)::value;
         asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
+        if constexpr (CKPT) {   // the state entering chunk c, for the backward pass
+            float* dst = a.states + ((size_t)bh * NC + c) * DK * DK + col0 + n;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dst[(size_t)((DK / 4) * w + 16 * mt + 4 * g + e) * DK + 16 * j] = S[j][mt][e];
+        }
         // S operand (B fragments) from the shared copy
         typename M::frag sb[NTW][O::NKD];
 #pragma unroll
@@ -381,31 +391,35 @@ inline int pick_ntw(int64_t BH, int NTALL) {
     return (NTALL % 2 == 0 && BH * (NTALL / 2) >= kCUs) ? 2 : 1;
 }
 
-template <typename E, int DK, int NTW, bool SUMMARY>
+template <typename E, int DK, int NTW, bool SUMMARY, bool CKPT>
 hipError_t launch_scan_n(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
     const int64_t groups = (BH + kXcds - 1) / kXcds;
     const int64_t blocks = groups * kXcds * (NTALL / NTW);
-    hipLaunchKernelGGL((kda_scan_kernel<E, DK, NTW, SUMMARY>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((kda_scan_kernel<E, DK, NTW, SUMMARY, CKPT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename E, int DK, bool SUMMARY>
+template <typename E, int DK, bool SUMMARY, bool CKPT = false>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
     if (BH == 0) return hipSuccess;
     switch (pick_ntw(BH, NTALL)) {
-    case 4: return launch_scan_n<E, DK, 4, SUMMARY>(a, s);
-    case 2: return launch_scan_n<E, DK, 2, SUMMARY>(a, s);
-    default: return launch_scan_n<E, DK, 1, SUMMARY>(a, s);
+    case 4: return launch_scan_n<E, DK, 4, SUMMARY, CKPT>(a, s);
+    case 2: return launch_scan_n<E, DK, 2, SUMMARY, CKPT>(a, s);
+    default: return launch_scan_n<E, DK, 1, SUMMARY, CKPT>(a, s);
     }
 }
 
 }  // namespace
 
 hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s) {
+    if (a.states) {   // forward pass that also keeps every chunk's entering state
+        if (bf16) return dk == 128 ? launch_scan_t<__bf16, 128, false, true>(a, s) : launch_scan_t<__bf16, 64, false, true>(a, s);
+        return dk == 128 ? launch_scan_t<float, 128, false, true>(a, s) : launch_scan_t<float, 64, false, true>(a, s);
+    }
     if (bf16) {
         if (dk == 128) return summary ? launch_scan_t<__bf16, 128, true>(a, s) : launch_scan_t<__bf16, 128, false>(a, s);
         return summary ? launch_scan_t<__bf16, 64, true>(a, s) : launch_scan_t<__bf16, 64, false>(a, s);

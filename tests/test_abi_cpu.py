@@ -123,8 +123,10 @@ def _bwd(L, pr, ws, **kw):
 def test_backward_workspace_and_argument_errors(L):
     p = _p()
     ws = L.kda_backward_workspace_size(ctypes.byref(p))
-    # per (b, h): 4 chunk checkpoints + 64 entering states, 128 x 128 fp32 each
-    assert ws == 2 * 3 * (4 + 64) * 128 * 128 * 4
+    # forward cards, reverse-pass cards (4 x 64x128 + 64x128 bf16 + 128 fp32),
+    # the forward output, and two fp32 states per chunk-head
+    chunks = 2 * 3 * 4
+    assert ws == chunks * 74240 + chunks * 82432 + 2 * 200 * 3 * 128 * 2 + 2 * chunks * 128 * 128 * 4
     assert L.kda_backward_workspace_size(ctypes.byref(_p(seqlen=0))) == 0
     assert L.kda_backward_workspace_size(ctypes.byref(_p(dk=96, dv=96))) == 0
     assert _bwd(L, None, ws) == 1
