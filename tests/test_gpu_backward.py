@@ -130,3 +130,30 @@ def test_backward_empty_sequence_passes_state_seed_through():
     gr = kda.backward(e, e, e, e, torch.empty(2, 0, 3, device=DEV), e, -0.1, d_state=ds)
     torch.cuda.synchronize()
     assert torch.equal(gr["dstate0"], ds)
+
+
+def test_bf16_backward_full_medium_workload_sampled_heads():
+    """The medium prefill workload at full size (B=4, T=4096, H=16, d=128,
+    bf16), in the same launch configuration the benchmark times; the oracle
+    adjoint runs on three sampled (row, head) pairs (heads are independent)."""
+    from kda_inputs import workload
+    inp = workload(1)
+    B, T, H, d = inp.q.shape[0], inp.q.shape[1], inp.q.shape[2], inp.q.shape[3]
+    rng = np.random.default_rng(4242)
+    do_io, do64 = _io(rng.standard_normal((B, T, H, d)), "bf16")
+    ds = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    dev = kda.to_device(inp)
+    note(f"[backward] full medium workload B={B} T={T} H={H} d={d} bf16")
+    gr = kda.backward(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["g"], inp.log_alpha_min,
+                      d_out=_dev(do_io, "bf16"), d_state=_dev(ds, "f32"))
+    torch.cuda.synchronize()
+    f = lambda a: to_f64(a, "bf16")
+    for b, h in [(0, 0), (2, 7), (3, 15)]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        ref = oracle.kda_grad(f(inp.q[sl]), f(inp.k[sl]), f(inp.v[sl]), inp.log_alpha[sl], inp.beta[sl], f(inp.g[sl]),
+                              inp.log_alpha_min, None, d_out=do64[sl], d_state=ds[b:b + 1, h:h + 1])
+        errs = {n: slice_err(gr[n][sl].float().cpu().numpy(), ref[n]) for n in TOKEN_GRADS}
+        errs["dstate0"] = slice_err(gr["dstate0"][b:b + 1, h:h + 1].cpu().numpy(), ref["dstate0"], token_major=False)
+        note(f"  (b={b}, h={h}) " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], (b, h, n, e)
