@@ -291,7 +291,8 @@ struct GradLds {
     static constexpr int LDC = C + 4;    // [C][C] rows
     static constexpr int LDB = NB + 4;   // [C][NB] rows
     static constexpr size_t K = 0;                          // k^ (zero on padded tokens)
-    static constexpr size_t Q = K + (size_t)C * LDK * 4;    // q^
+    static constexpr size_t Q = K + (size_t)C * LDK * 4;    // q^; during the column loop, the block of S0 and dS
+    static constexpr int LDSB = NB + 4;                     // [DK][NB] rows of the staged state blocks
     static constexpr size_t EG = Q + (size_t)C * LDK * 4;   // e^gamma
     static constexpr size_t P = EG + (size_t)C * LDK * 4;   // P, then dP, then dgamma (spans P and T)
     static constexpr size_t T = P + (size_t)C * LDC * 4;    // diag(beta) A -> T, then dA
@@ -302,8 +303,11 @@ struct GradLds {
     static constexpr size_t BETA = DU + (size_t)C * LDB * 4;
     static constexpr size_t NK = BETA + (size_t)C * 4;      // |k|
     static constexpr size_t NQ = NK + (size_t)C * 4;        // |q|
-    static constexpr size_t DGC = NQ + (size_t)C * 4;       // [5][DK]: per-wave sum dKe*Ke, rowsum(S0*dS)
+    static constexpr size_t RK = NQ + (size_t)C * 4;        // 1 / max(|k|, 1e-6)
+    static constexpr size_t RQ = RK + (size_t)C * 4;        // 1 / max(|q|, 1e-6)
+    static constexpr size_t DGC = RQ + (size_t)C * 4;       // [5][DK]: per-wave sum dKe*Ke, rowsum(S0*dS)
     static constexpr size_t BYTES = DGC + (size_t)5 * DK * 4;
+    static_assert(2 * DK * LDSB <= C * LDK, "state blocks fit over q^");
     static_assert((size_t)C * LDK <= 2 * (size_t)C * LDC, "dgamma fits over P and T");
 };
 
@@ -330,6 +334,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
     float* sBeta = reinterpret_cast<float*>(lds + LY::BETA);
     float* sNk = reinterpret_cast<float*>(lds + LY::NK);
     float* sNq = reinterpret_cast<float*>(lds + LY::NQ);
+    float* sRk = reinterpret_cast<float*>(lds + LY::RK);
+    float* sRq = reinterpret_cast<float*>(lds + LY::RQ);
+    float* sS0 = sQ;                       // [DK][LDSB]: S0, this block's columns
+    float* sDS = sQ + DK * LY::LDSB;       // [DK][LDSB]: dS, this block's columns
+    constexpr int LDSB = LY::LDSB;
     float* sDGC = reinterpret_cast<float*>(lds + LY::DGC);
     float* sDG = sP;
 
@@ -355,6 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
     const E* kp = reinterpret_cast<const E*>(a.k);
 
     // ---- 1: norms, k^, q^, e^gamma, beta ----
+#pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
         const int i = 16 * w + ii;
         const size_t r = rowi(i);
@@ -373,23 +383,40 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         if (lane == 0) {
             sNk[i] = sqrtf(sk);
             sNq[i] = sqrtf(sq);
+            sRk[i] = 1.f / fmaxf(sqrtf(sk), 1e-6f);
+            sRq[i] = 1.f / fmaxf(sqrtf(sq), 1e-6f);
         }
     }
     if (t < C) sBeta[t] = t < nvalid ? a.beta[rowi(t)] : 0.f;
     for (int idx = t; idx < C * LDC; idx += kThreads) sT[idx] = 0.f;   // T's upper tiles stay zero
     __syncthreads();
-    for (int idx = t; idx < C * DK; idx += kThreads) {
-        const int i = idx / DK, ch = idx % DK;
-        const size_t r = rowi(i);
+    // q^ (zero on padded tokens), four channels per item
+    auto load_qhat = [&]() {
+        for (int idx = t; idx < C * DK / 4; idx += kThreads) {
+            const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
+            const f32x4 x = ld4(qp + rowi(i) * DK + ch);
+            st4(sQ + i * LDK + ch, i < nvalid ? x * sRq[i] : f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+    };
+    load_qhat();
+    for (int idx = t; idx < C * DK / 4; idx += kThreads) {
+        const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
+        const size_t r = rowi(i) * DK + ch;
         const bool ok = i < nvalid;
-        sK[i * LDK + ch] = ok ? to_f32(kp[r * DK + ch]) / fmaxf(sNk[i], 1e-6f) : 0.f;
-        sQ[i * LDK + ch] = ok ? to_f32(qp[r * DK + ch]) / fmaxf(sNq[i], 1e-6f) : 0.f;
+        const f32x4 x = ld4(kp + r);
+        const f32x4 la = *reinterpret_cast<const f32x4*>(a.log_alpha + r);
+        st4(sK + i * LDK + ch, ok ? x * sRk[i] : f32x4{0.f, 0.f, 0.f, 0.f});
+        // floored log-decay in base 2 (padded tokens add nothing)
+        f32x4 lam;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lam[e] = ok ? fmaxf(la[e], a.floor_) * kLog2e : 0.f;
+        st4(sEG + i * LDK + ch, lam);
     }
-    if (t < DK) {   // cumulative log-decay of channel t (base 2), padded tokens add nothing
+    __syncthreads();
+    if (t < DK) {   // e^gamma: cumulative log-decay of channel t
         float run = 0.f;
         for (int i = 0; i < C; ++i) {
-            const float la = a.log_alpha[rowi(i) * DK + t];
-            run += i < nvalid ? fmaxf(la, a.floor_) * kLog2e : 0.f;
+            run += sEG[i * LDK + t];
             sEG[i * LDK + t] = __builtin_amdgcn_exp2f(run);
         }
     }
@@ -405,6 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
     for (int j = 0; j < 4; ++j) {
         if (j <= w) {
             f32x4 xa = {0.f, 0.f, 0.f, 0.f}, xp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
             for (int s = 0; s < NKD; ++s) {
                 const float kh = Kh(16 * j + n, 4 * s + g);
                 xa = mma_f32(Kt(16 * w + n, 4 * s + g), kh, xa);
@@ -481,8 +509,26 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
 #pragma unroll
     for (int j = 0; j < 4; ++j) dMa[j] = dPa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 dbp = {0.f, 0.f, 0.f, 0.f};
+    constexpr int NSI = (DK * NB / 4 + kThreads - 1) / kThreads;   // staged 4-float pieces per thread
+    float rowp[NSI];   // rowsum(S0 * dS) over the blocks so far, row (idx / 4) of piece idx
+#pragma unroll
+    for (int j = 0; j < NSI; ++j) rowp[j] = 0.f;
     for (int vb = 0; vb < DV / NB; ++vb) {
         const int col0 = NB * vb;
+        // S0 and dS, this block's columns, to LDS (q^ is reloaded after the loop)
+#pragma unroll
+        for (int j = 0; j < NSI; ++j) {
+            const int idx = t + j * kThreads;
+            if (idx < DK * NB / 4) {
+                const int row = idx / (NB / 4), c4 = (idx % (NB / 4)) * 4;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(S0 + (size_t)row * DV + col0 + c4);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(dSo + (size_t)row * DV + col0 + c4);
+                st4(sS0 + row * LDSB + c4, x);
+                st4(sDS + row * LDSB + c4, y);
+                rowp[j] += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+            }
+        }
+        __syncthreads();
         // R = V - Kt S0 (rows 16w.., this block's columns)
         f32x4 r;
 #pragma unroll
@@ -490,7 +536,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
             const int i = 16 * w + 4 * g + e;
             r[e] = i < nvalid ? to_f32(vp[rowi(i) * DV + col0 + n]) : 0.f;
         }
-        for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w + n, 4 * s + g), S0[(size_t)(4 * s + g) * DV + col0 + n], r);
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
         // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g))
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -511,7 +558,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         for (int e = 0; e < 4; ++e) sU[(16 * w + 4 * g + e) * LDB + n] = u[e];
         // dU = Ke dS + P^T dO (P^T upper triangular)
         f32x4 du = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w + n, 4 * s + g), dSo[(size_t)(4 * s + g) * DV + col0 + n], du);
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
         for (int s = 4 * w; s < NKC; ++s) du = mma_f32(sP[(4 * s + g) * LDC + 16 * w + n], sDO[(4 * s + g) * LDB + n], du);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sDU[(16 * w + 4 * g + e) * LDB + n] = du[e];
@@ -549,8 +597,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
             const float au = sU[(16 * w + n) * LDB + 4 * s + g];
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                const size_t si = (size_t)(16 * ct + n) * DV + col0 + 4 * s + g;
-                const float b0 = S0[si], b1 = dSo[si];
+                const int si = (16 * ct + n) * LDSB + 4 * s + g;
+                const float b0 = sS0[si], b1 = sDS[si];
                 dQt[ct] = mma_f32(ao, b0, dQt[ct]);
                 dKt[ct] = mma_f32(ar, b0, dKt[ct]);
                 dKe[ct] = mma_f32(au, b1, dKe[ct]);
@@ -559,6 +607,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         __syncthreads();
     }
 
+    // rowsum(S0 * dS): the four pieces of a row sit in adjacent lanes; q^ back over the state blocks
+#pragma unroll
+    for (int j = 0; j < NSI; ++j) {
+        float x = rowp[j];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        const int idx = t + j * kThreads;
+        if (idx < DK * NB / 4 && (idx & 3) == 0) sDGC[4 * DK + idx / (NB / 4)] = x;
+    }
+    load_qhat();
+
     // ---- 5: dbeta; dA and dP to LDS ----
     {
         f32x4 db = dbp;
@@ -566,6 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         for (int j = 0; j < 4; ++j) {
             if (j <= w) {   // A tile (w, j) again, for sum_j dM_ij A_ij
                 f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
                 for (int s = 0; s < NKD; ++s) xa = mma_f32(Kt(16 * w + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), xa);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -675,33 +735,33 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
             }
         }
     }
-    // ---- 9: dgamma to LDS (over dP and dA), rowsum(S0 * dS) per key channel ----
+    // ---- 9: dgamma to LDS (over dP and dA) ----
     __syncthreads();
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sDG[(16 * w + 4 * g + e) * LDK + 16 * ct + n] = dKh[ct][e];
-    for (int ch = w; ch < DK; ch += 4) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < DV / 64; ++e) {
-            const size_t si = (size_t)ch * DV + lane * (DV / 64) + e;
-            s += S0[si] * dSo[si];
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off);
-        if (lane == 0) sDGC[4 * DK + ch] = s;
-    }
+
     __syncthreads();
     // ---- 10: dlog_alpha = reverse cumulative sum of dgamma (zero where the floor binds) ----
-    if (t < DK) {
-        const float egc = sEG[(C - 1) * LDK + t];
-        float acc = sDGC[t] + sDGC[DK + t] + sDGC[2 * DK + t] + sDGC[3 * DK + t] + egc * sDGC[4 * DK + t];
+    if (t < DK) {   // in place, channel t
+        float acc = sDGC[t] + sDGC[DK + t] + sDGC[2 * DK + t] + sDGC[3 * DK + t] +
+                    sEG[(C - 1) * LDK + t] * sDGC[4 * DK + t];
         for (int i = nvalid - 1; i >= 0; --i) {
             acc += sDG[i * LDK + t];
-            const size_t ri = rowi(i) * DK + t;
-            a.dlog_alpha[ri] = a.log_alpha[ri] > a.floor_ ? acc : 0.f;
+            sDG[i * LDK + t] = acc;
         }
+    }
+    __syncthreads();
+    for (int idx = t; idx < nvalid * (DK / 4); idx += kThreads) {
+        const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
+        const size_t r = rowi(i) * DK + ch;
+        const f32x4 la = *reinterpret_cast<const f32x4*>(a.log_alpha + r);
+        const f32x4 acc = *reinterpret_cast<const f32x4*>(sDG + i * LDK + ch);
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = la[e] > a.floor_ ? acc[e] : 0.f;
+        *reinterpret_cast<f32x4*>(a.dlog_alpha + r) = y;
     }
 }
 
