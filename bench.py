@@ -1,6 +1,7 @@
 """KDA benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-segmented] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-segmented] [--no-backward]
+                    [--no-cpu-baseline]
 
 A step is one chunked prefill (update-card preparation + ordered hand-off
 with the gated read-out) of the long-prefill workload: B=1, T=65,536, H=32,
@@ -21,6 +22,9 @@ Also reported on the same JSON line:
   * the segmented (context-parallel) prefill of 1,048,576 tokens x 8 heads as
     16 segments: per-call times of prepare, segment summaries, in-order
     combine and the per-segment recompute;
+  * the backward pass (gradients of every prefill input and of the initial
+    state) on the medium prefill workload B=4, T=4,096, H=16, d=128 bf16:
+    ms per call and token-heads/s, beside the forward on the same inputs;
   * cpu_baseline: the fp64 oracle timed on a bounded sample on the host.
 """
 from __future__ import annotations
@@ -78,6 +82,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-segmented", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -296,6 +301,53 @@ def main():
                      "scan": SCAN_BYTES * ths / (times["scan"] * 1e-3) / 1e9},
         }
         del ds, wss, outs
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- backward
+    if not args.no_backward and not args.decode_only:
+        Wb = WORKLOADS[1]
+        inp = workload(1)
+        db = kda.to_device(inp, dev)
+        floor_b = inp.log_alpha_min
+        Bb, Tb, Hb = Wb["B"], Wb["T"], Wb["H"]
+        gen = torch.Generator(device=dev).manual_seed(11)
+        d_out = torch.randn((Bb, Tb, Hb, D), device=dev, generator=gen).to(torch.bfloat16)
+        d_state = torch.randn((Bb, Hb, D, D), device=dev, generator=gen)
+        pb = kda.problem(Bb, Tb, Hb, D, D, kda.KDA_BF16, floor_b)
+        wsb = torch.empty(kda.backward_workspace_size(pb), dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return kda.backward(db["q"], db["k"], db["v"], db["log_alpha"], db["beta"], db["g"], floor_b,
+                                d_out=d_out, d_state=d_state, workspace=wsb)
+
+        def fstep():
+            return kda.prefill(db["q"], db["k"], db["v"], db["log_alpha"], db["beta"], db["g"], floor_b)
+
+        bstep(); fstep()
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            bstep()
+        e1.record()
+        for _ in range(reps):
+            fstep()
+        e2.record()
+        torch.cuda.synchronize()
+        bms, fms = e0.elapsed_time(e1) / reps, e1.elapsed_time(e2) / reps
+        th = Bb * Tb * Hb
+        # algorithmic bytes per token-head: q,k,v,g,d_out in (bf16), log_alpha,
+        # beta in (fp32); dq,dk,dv,dg out (bf16), dlog_alpha, dbeta out (fp32)
+        bwd_bytes = 5 * D * 2 + D * 4 + 4 + 4 * D * 2 + D * 4 + 4
+        # gradient-kernel products per token-head: five C x d x d (with a state), nine C x C x d
+        bwd_flop = 5 * 2 * D * D + 9 * 2 * C * D
+        log(f"[bench] backward {bms:.3f} ms, forward {fms:.3f} ms on {Wb['name']}")
+        result["backward"] = {"workload": Wb["name"], "ms": bms, "forward_ms": fms, "ratio_to_forward": bms / fms,
+                              "token_heads_per_s": th / (bms * 1e-3), "GBps": bwd_bytes * th / (bms * 1e-3) / 1e9,
+                              "bytes_per_token_head": bwd_bytes, "grad_flop_per_token_head": bwd_flop,
+                              "grad_TFLOPs_over_whole_call": bwd_flop * th / (bms * 1e-3) / 1e12}
+        del db, wsb, d_out, d_state
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- cpu baseline
