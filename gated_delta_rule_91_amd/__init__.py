@@ -8,8 +8,9 @@ CPU or PyTorch fallback: if the library is missing, every call raises.
 
 Entry points (same names as the C ABI, minus the ``kda_`` prefix):
     workspace_size, chunk_prepare, chunk_scan, segment_summarize,
-    segment_combine, decode_step, backward_workspace_size, backward
-Conveniences built from them: prefill, segmented_prefill.
+    segment_combine, decode_step, backward_workspace_size, backward,
+    varlen_workspace_size, varlen_prepare, varlen_scan
+Conveniences built from them: prefill, segmented_prefill, varlen_prefill.
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "w
           4: "HIP runtime error"}
 EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_segment_summarize",
            "kda_segment_combine", "kda_decode_step", "kda_backward_workspace_size", "kda_backward",
-           "kda_status_string")
+           "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -63,8 +64,12 @@ def lib() -> ctypes.CDLL:
         L.kda_backward_workspace_size.argtypes = [PP]
         L.kda_backward_workspace_size.restype = SZ
         L.kda_backward.argtypes = [PP] + [P] * 16 + [P, SZ, P]
+        L.kda_varlen_workspace_size.argtypes = [PP, I64]
+        L.kda_varlen_workspace_size.restype = SZ
+        L.kda_varlen_prepare.argtypes = [PP, I64, P, P, P, P, P, P, P, SZ, P]
+        L.kda_varlen_scan.argtypes = [PP, I64, P, P, SZ, P, P, P, P, P]
         for f in EXPORTS[1:-1]:
-            if f != "kda_backward_workspace_size":
+            if not f.endswith("workspace_size"):
                 getattr(L, f).restype = I32
         L.kda_status_string.argtypes = [I32]
         L.kda_status_string.restype = ctypes.c_char_p
@@ -221,6 +226,59 @@ def backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, d
         _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace), workspace.numel(),
         _stream(stream)))
     return r
+
+
+def varlen_workspace_size(p: KdaProblem, n_seq: int) -> int:
+    n = lib().kda_varlen_workspace_size(ctypes.byref(p), n_seq)
+    if n == 0 and n_seq > 0:
+        raise KdaError("kda_varlen_workspace_size", 2)
+    return n
+
+
+def _cu(cu_seqlens):
+    torch = _torch()
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    return cu_seqlens.numel() - 1
+
+
+def varlen_prepare(q, k, v, log_alpha, beta, log_alpha_min: float, cu_seqlens, workspace=None, stream=None):
+    """Stage 1 for a packed batch: q, k, v, log_alpha [1, T, H, d], beta [1, T, H];
+    cu_seqlens int32 [n_seq+1] on the device.  Returns the workspace."""
+    torch = _torch()
+    p = _problem_of(q, v, log_alpha_min)
+    n_seq = _cu(cu_seqlens)
+    nbytes = varlen_workspace_size(p, n_seq)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check("kda_varlen_prepare", lib().kda_varlen_prepare(
+        ctypes.byref(p), n_seq, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def varlen_scan(workspace, g, log_alpha_min: float, cu_seqlens, state_in=None, out=None, state_out=None,
+                want_state: bool = True, stream=None):
+    """Stage 2 for a packed batch.  Returns (out [1, T, H, dv], state_out [n_seq, H, dk, dv])."""
+    torch = _torch()
+    B, T, H, dv = g.shape
+    p = problem(B, T, H, dv, dv, _io_code(g.dtype), log_alpha_min)
+    n_seq = _cu(cu_seqlens)
+    if out is None:
+        out = torch.empty_like(g)
+    if state_out is None and want_state:
+        state_out = torch.empty((n_seq, H, dv, dv), dtype=torch.float32, device=g.device)
+    _check("kda_varlen_scan", lib().kda_varlen_scan(
+        ctypes.byref(p), n_seq, _ptr(cu_seqlens), _ptr(workspace), workspace.numel(), _ptr(g), _ptr(state_in),
+        _ptr(out), _ptr(state_out), _stream(stream)))
+    return out, state_out
+
+
+def varlen_prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, cu_seqlens, state_in=None, workspace=None,
+                   stream=None):
+    """Chunked prefill of a packed variable-length batch.  Returns (out, final states [n_seq, H, dk, dv])."""
+    ws = varlen_prepare(q, k, v, log_alpha, beta, log_alpha_min, cu_seqlens, workspace=workspace, stream=stream)
+    return varlen_scan(ws, g, log_alpha_min, cu_seqlens, state_in=state_in, stream=stream)
 
 
 def prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, workspace=None, stream=None):

@@ -53,6 +53,19 @@ kda_status device_ready() {
 
 kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// Packed variable-length batches: chunk offsets first, then the cards.
+size_t varlen_offsets_bytes(int64_t n_seq) { return ((size_t)(n_seq + 1) * 8 + 255) / 256 * 256; }
+int64_t varlen_max_chunks(const kda_problem* p, int64_t n_seq) { return n_chunks(p) + n_seq; }
+
+kda_status check_varlen(const kda_problem* p, int64_t n_seq) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    if (p->batch != 1 || n_seq < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if ((varlen_max_chunks(p, n_seq) + 1) * (int64_t)p->heads > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (n_seq * (int64_t)p->heads * (p->dv / 16) > (int64_t)INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,7 +98,7 @@ kda_status kda_chunk_prepare(const kda_problem* p, const void* q, const void* k,
     if (workspace_bytes < kda_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (!nonempty) return KDA_OK;
     if ((st = device_ready()) != KDA_OK) return st;
-    PrepareArgs a;
+    PrepareArgs a = {};
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.ws = static_cast<char*>(workspace);
     a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p);
@@ -166,6 +179,55 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.g = g; a.state = state; a.out = out;
     a.N = N; a.H = H; a.floor_ = log_alpha_min;
     return hip_status(launch_decode(io_dtype == KDA_BF16, dk, a, (hipStream_t)stream));
+}
+
+size_t kda_varlen_workspace_size(const kda_problem* p, int64_t n_seq) {
+    if (check_varlen(p, n_seq) != KDA_OK || n_seq == 0) return 0;
+    return varlen_offsets_bytes(n_seq) +
+           (size_t)varlen_max_chunks(p, n_seq) * (size_t)p->heads * card_bytes(p->io_dtype == KDA_BF16, p->dk);
+}
+
+kda_status kda_varlen_prepare(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens, const void* q,
+                              const void* k, const void* v, const float* log_alpha, const float* beta,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status st = check_varlen(p, n_seq);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->seqlen > 0;
+    if (!ok_beta(cu_seqlens, n_seq > 0) || !ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) ||
+        !ok_ptr(log_alpha, tokens) || !ok_beta(beta, tokens) || !ok_ptr(workspace, n_seq > 0))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_varlen_workspace_size(p, n_seq)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (n_seq == 0) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    PrepareArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+    a.chunk_off = static_cast<int64_t*>(workspace);
+    a.ws = static_cast<char*>(workspace) + varlen_offsets_bytes(n_seq);
+    a.cu_seqlens = cu_seqlens;
+    a.B = n_seq; a.T = p->seqlen; a.H = p->heads; a.NC = 0;
+    a.floor_ = p->log_alpha_min;
+    return hip_status(launch_prepare(p->io_dtype == KDA_BF16, p->dk, a, (hipStream_t)stream));
+}
+
+kda_status kda_varlen_scan(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens, const void* workspace,
+                           size_t workspace_bytes, const void* g, const float* state_in, void* out, float* state_out,
+                           void* stream) {
+    kda_status st = check_varlen(p, n_seq);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->seqlen > 0;
+    if (!ok_beta(cu_seqlens, n_seq > 0) || !ok_ptr(workspace, n_seq > 0) || !ok_ptr(g, tokens) ||
+        !ok_ptr(out, tokens) || !ok_opt_ptr(state_in) || !ok_opt_ptr(state_out))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_varlen_workspace_size(p, n_seq)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (n_seq == 0 || (!tokens && !state_out)) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    ScanArgs a = {};
+    a.chunk_off = static_cast<const int64_t*>(workspace);
+    a.ws = static_cast<const char*>(workspace) + varlen_offsets_bytes(n_seq);
+    a.cu_seqlens = cu_seqlens;
+    a.g = g; a.state_in = state_in; a.out = out; a.state_out = state_out;
+    a.B = n_seq; a.T = p->seqlen; a.H = p->heads; a.NC = 0;
+    return hip_status(launch_scan(p->io_dtype == KDA_BF16, p->dk, false, a, (hipStream_t)stream));
 }
 
 size_t kda_backward_workspace_size(const kda_problem* p) {

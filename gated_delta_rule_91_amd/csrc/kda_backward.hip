@@ -793,7 +793,7 @@ size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk) 
 hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t s) {
     const BwdLayout L(bf16, a.B, a.T, a.H, dk);
     if (a.NC > 0 && a.B > 0) {   // forward cards, then the forward hand-off keeping every chunk's entering state
-        PrepareArgs p;
+        PrepareArgs p = {};
         p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.beta = a.beta;
         p.ws = a.ws + L.cards;
         p.B = a.B; p.T = a.T; p.H = a.H; p.NC = a.NC; p.floor_ = a.floor_;

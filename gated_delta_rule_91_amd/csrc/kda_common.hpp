@@ -127,6 +127,43 @@ struct Card {
     static constexpr size_t BYTES = ((GC + (size_t)DK * sizeof(float)) + 255) / 256 * 256;
 };
 
+// Where one (sequence, head)'s tokens and cards are.
+//  * Uniform batch: row b holds T tokens starting at token b*T; its chunks'
+//    cards start at card (b*H + h)*NC.
+//  * Packed variable-length batch: sequence s holds tokens [cu[s], cu[s+1])
+//    of one packed row (offsets clamped into [0, T], so no offset array can
+//    send an access outside the arrays); its NC_s chunks' cards start at
+//    card chunk_off[s]*H + h*NC_s, chunk_off being the prefix sum of NC_s.
+struct SeqSpan {
+    int64_t tok0;    // first token (row index along the packed token axis)
+    int64_t len;     // tokens
+    int nc;          // chunks
+    int64_t card0;   // card index of chunk 0 of (sequence, head)
+};
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int64_t s, int64_t T, int64_t& st, int64_t& en) {
+    const int64_t a = cu[s], b = cu[s + 1];
+    st = a < 0 ? 0 : (a > T ? T : a);
+    en = b < st ? st : (b > T ? T : b);
+}
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, const int64_t* chunk_off, int64_t T, int NC,
+                                            int64_t b, int h, int H) {
+    SeqSpan r;
+    if (cu) {
+        int64_t st, en;
+        seq_bounds(cu, b, T, st, en);
+        r.tok0 = st;
+        r.len = en - st;
+        r.nc = (int)(chunk_off[b + 1] - chunk_off[b]);
+        r.card0 = chunk_off[b] * H + (int64_t)h * r.nc;
+    } else {
+        r.tok0 = b * T;
+        r.len = T;
+        r.nc = NC;
+        r.card0 = (b * H + h) * (int64_t)NC;
+    }
+    return r;
+}
+
 // Element index of (row, k) of an A operand with K columns in fragment order.
 template <typename E>
 __host__ __device__ constexpr int frag_index(int row, int k, int K) {

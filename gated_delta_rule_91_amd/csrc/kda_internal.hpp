@@ -16,9 +16,11 @@ struct PrepareArgs {
     const float* log_alpha;
     const float* beta;
     char* ws;
-    int64_t B, T;
+    int64_t B, T;            // packed variable-length batches: B = sequences, T = packed tokens
     int H, NC;
     float floor_;
+    const int32_t* cu_seqlens;   // or null (uniform batch); else [B+1] token offsets
+    int64_t* chunk_off;          // with cu_seqlens: [B+1] first chunk of each sequence (written here)
 };
 
 struct ScanArgs {
@@ -30,8 +32,10 @@ struct ScanArgs {
     float* transition;       // summary mode: [B,H,dk,dk]
     float* zero_state;       // summary mode: [B,H,dk,dv]
     float* states;           // or null; else the state entering every chunk, [B,H,NC,dk,dv]
-    int64_t B, T;
+    int64_t B, T;            // packed variable-length batches: B = sequences, T = packed tokens
     int H, NC;
+    const int32_t* cu_seqlens;   // or null (uniform batch); else [B+1] token offsets
+    const int64_t* chunk_off;    // with cu_seqlens: [B+1] first chunk of each sequence
 };
 
 struct DecodeArgs {

@@ -110,29 +110,44 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index (uniform)
 
     // block -> (b, chunk, h): heads fastest, so neighbouring workgroups read
-    // neighbouring pieces of the same token rows
-    const int H = a.H, NC = a.NC;
-    const int64_t T = a.T;
+    // neighbouring pieces of the same token rows.  Packed variable-length
+    // batches number chunks across all sequences (chunk_off, written by the
+    // plan kernel); workgroups past the last chunk have nothing to do.
+    const int H = a.H;
     const int64_t wg = blockIdx.x;
     const int h = (int)(wg % H);
     const int64_t rest = wg / H;
-    const int c = (int)(rest % NC);
-    const int64_t b = rest / NC;
+    int64_t b;
+    int c;
+    if (a.cu_seqlens) {
+        if (rest >= a.chunk_off[a.B]) return;
+        int64_t lo = 0, hi = a.B - 1;   // the sequence holding global chunk `rest`
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (a.chunk_off[mid] <= rest) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        c = (int)(rest - a.chunk_off[lo]);
+    } else {
+        c = (int)(rest % a.NC);
+        b = rest / a.NC;
+    }
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.NC, b, h, H);
     const int64_t tok0 = (int64_t)c * C;
-    char* card = a.ws + (((size_t)b * H + h) * NC + c) * CL::BYTES;
+    char* card = a.ws + (size_t)(sp.card0 + c) * CL::BYTES;
 
     // ---------------- phase A ----------------
     // Log-decay is carried in base-2 units (lambda * log2 e) so every
     // exponential is a single v_exp_f32; e^-gamma comes from v_rcp_f32.
     const int cp = t % CP, c0 = 2 * cp;
     const int grp = (CP == 64) ? w : t / CP;   // at d_k = 128 a token group is a wave
-    const size_t row0 = ((size_t)b * T + tok0) * H + h;
+    const size_t row0 = (size_t)(sp.tok0 + tok0) * H + h;
     const size_t tstride = (size_t)H * DK;
     const float* la_b = a.log_alpha + row0 * DK;
     const E* q_b = reinterpret_cast<const E*>(a.q) + row0 * DK;
     const E* k_b = reinterpret_cast<const E*>(a.k) + row0 * DK;
     const E* v_b = reinterpret_cast<const E*>(a.v) + row0 * DK;
-    const int nvalid = (int)((T - tok0) < C ? (T - tok0) : C);
+    const int nvalid = (int)((sp.len - tok0) < C ? (sp.len - tok0) : C);
     // Loads are unconditional: a padded token re-reads the last valid row (a
     // load under a branch would be followed by a wait on every outstanding
     // load).  Padding is an exact identity step as long as its beta and
@@ -403,9 +418,48 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     store_frag_order<E, C, DK>(card + CL::WK, sWk, LDR, t);   // Wk -> card
 }
 
+// Chunk offsets of a packed variable-length batch: chunk_off[s] = sum of
+// ceil(len/C) over the sequences before s (one workgroup, a block-wide scan
+// per 256 sequences).
+__global__ __launch_bounds__(kThreads) void kda_varlen_plan_kernel(const int32_t* cu, int64_t nseq, int64_t T,
+                                                                  int64_t* chunk_off) {
+    __shared__ int64_t part[kThreads];
+    const int t = threadIdx.x;
+    if (t == 0) chunk_off[0] = 0;
+    int64_t carry = 0;
+    for (int64_t base = 0; base < nseq; base += kThreads) {
+        const int64_t s = base + t;
+        int64_t ncs = 0;
+        if (s < nseq) {
+            int64_t st, en;
+            seq_bounds(cu, s, T, st, en);
+            ncs = (en - st + kChunk - 1) / kChunk;
+        }
+        part[t] = ncs;
+        __syncthreads();
+        for (int d = 1; d < kThreads; d <<= 1) {
+            const int64_t x = t >= d ? part[t - d] : 0;
+            __syncthreads();
+            part[t] += x;
+            __syncthreads();
+        }
+        if (s < nseq) chunk_off[s + 1] = carry + part[t];
+        carry += part[kThreads - 1];
+        __syncthreads();
+    }
+}
+
 template <typename E, int DK>
 hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t s) {
-    const int64_t blocks = a.B * (int64_t)a.H * a.NC;
+    if (a.cu_seqlens) {
+        if (a.B == 0) return hipSuccess;
+        hipLaunchKernelGGL(kda_varlen_plan_kernel, dim3(1), dim3(kThreads), 0, s, a.cu_seqlens, a.B, a.T, a.chunk_off);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // packed batches: an upper bound on the chunk count (sum of ceil(len/C) <= ceil(T/C) + B)
+    const int64_t chunks = a.cu_seqlens ? (a.T + kChunk - 1) / kChunk + a.B : a.B * (int64_t)a.NC;
+    const int64_t blocks = chunks * a.H;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((kda_prepare_kernel<E, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4, n = lane & 15;
 
     // XCD-aware chain decode
-    const int H = a.H, NC = a.NC;
+    const int H = a.H;
     const int64_t BH = a.B * (int64_t)H;
     const int64_t x = blockIdx.x;
     const int xcd = (int)(x % kXcds);
@@ -178,6 +178,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     if (bh >= BH) return;
     const int64_t b = bh / H;
     const int h = (int)(bh % H);
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.NC, b, h, H);
+    const int NC = sp.nc;
+    const int64_t Tl = sp.len;   // this sequence's tokens
     const bool vcols = tile0 < NT;                        // value columns (else transition columns)
     const int col0 = (vcols ? tile0 : tile0 - NT) * 16;   // first column of this workgroup
 
@@ -204,11 +207,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MTS; ++mt) st4(sS + (16 * j + n) * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, S[j][mt]);
 
-    const char* cards = a.ws + (size_t)bh * NC * CL::BYTES;
+    const char* cards = a.ws + (size_t)sp.card0 * CL::BYTES;
     const LaneOff<E, DK, NTW> lo(w, g, n, lane, tile0, vcols);
     const uint32_t rsb = (uint32_t)(H * DK * (int)sizeof(E));              // bytes between tokens
     // first token row of this (b, h) at column col0, as bytes, for g and out
-    const size_t head0 = (((size_t)b * a.T * H + h) * DK + col0) * sizeof(E);
+    const size_t head0 = (((size_t)sp.tok0 * H + h) * DK + col0) * sizeof(E);
     const char* gseq = reinterpret_cast<const char*>(a.g) + head0;
     char* oseq = reinterpret_cast<char*>(a.out) + head0;
 
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     auto load = [&](O& o, int c) {
         const int cc = c < NC ? c : NC - 1;
         const int64_t t0 = (int64_t)cc * C;
-        const int nvalid = (int)(a.T - t0 < C ? a.T - t0 : C);
+        const int nvalid = (int)(Tl - t0 < C ? Tl - t0 : C);
         load_ops<E, DK, NTW, SUMMARY>(o, cards + (size_t)cc * CL::BYTES, lo, gseq + (size_t)t0 * rsb, rsb, nvalid);
         const int cp = c + kPrefetch < NC ? c + kPrefetch : NC - 1;
         o.pf = ldc<uint32_t>(cards + (size_t)cp * CL::BYTES, poff);
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
 
         if (!SUMMARY) {
             char* ochunk = oseq + (size_t)c * C * rsb;
-            const int nvalid = (int)(a.T - (int64_t)c * C < C ? a.T - (int64_t)c * C : C);
+            const int nvalid = (int)(Tl - (int64_t)c * C < C ? Tl - (int64_t)c * C : C);
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 // O^T (16 columns x this wave's 16 tokens) = S_old^T Qt^T + U^T P^T.
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     if (NC > 0) {
         using Full = std::integral_constant<bool, true>;
         using Part = std::integral_constant<bool, false>;
-        const int NCF = (int64_t)NC * C > a.T ? NC - 1 : NC;   // full chunks
+        const int NCF = (int64_t)NC * C > Tl ? NC - 1 : NC;   // full chunks
         O o0, o1, o2, o3;
         load(o0, 0);
         load(o1, 1);

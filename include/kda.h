@@ -129,6 +129,34 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
                            const float* log_alpha, const float* beta, const void* g,
                            float* state, void* out, void* stream);
 
+/* Packed variable-length batches: n_seq sequences of different lengths packed
+ * back to back along the token axis of one row, as serving batches requests
+ * that each carry their own fixed-size state [devpress.csdn.net K3 article
+ * §十六: per-request recursive state instead of a growing cache].  The problem
+ * p has batch == 1 and seqlen == the packed token count; sequence s is tokens
+ * [cu_seqlens[s], cu_seqlens[s+1]) (cu_seqlens: device int32 [n_seq+1],
+ * non-decreasing, from 0 to seqlen; values outside [0, seqlen] are clamped,
+ * so no offset array makes an access leave the arrays).  Chunks never straddle
+ * two sequences, and every sequence's tail is padded inside the kernels.
+ *
+ * Workspace bytes: chunk offsets plus at most ceil(seqlen/C) + n_seq chunks'
+ * cards per head.  Returns 0 if p is invalid or unsupported (batch != 1), or
+ * if n_seq is 0. */
+size_t kda_varlen_workspace_size(const kda_problem* p, int64_t n_seq);
+
+/* kda_chunk_prepare for a packed batch (same arrays, [1, seqlen, H, d]). */
+kda_status kda_varlen_prepare(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
+                              const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, void* workspace, size_t workspace_bytes, void* stream);
+
+/* kda_chunk_scan for a packed batch, with the workspace kda_varlen_prepare
+ * filled for the same p, n_seq and cu_seqlens.  g, out: [1, seqlen, H, dv];
+ * state_in, state_out: [n_seq, H, dk, dv] fp32 or NULL (state_out may equal
+ * state_in); an empty sequence passes its state_in through. */
+kda_status kda_varlen_scan(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
+                           const void* workspace, size_t workspace_bytes, const void* g,
+                           const float* state_in, void* out, float* state_out, void* stream);
+
 /* Bytes of scratch kda_backward needs for problem p: the state entering every
  * chunk plus the 64 states entering one chunk's tokens, fp32, per (b, h).
  * Returns 0 if p is invalid or unsupported, or if p has no tokens. */

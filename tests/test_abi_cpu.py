@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -142,6 +142,30 @@ def test_backward_workspace_and_argument_errors(L):
     none = {n: None for n in ["q", "k", "v", "la", "b", "g", "dq", "dk", "dv", "dla", "db", "dg", "w"]}
     assert _bwd(L, _p(batch=0), 0, ds0=None, **none) == 0
     assert _bwd(L, _p(seqlen=0), 0, ds0=None, **none) == 0
+
+
+def test_varlen_workspace_and_argument_errors(L):
+    p = _p(batch=1, seqlen=1000)
+    # chunk offsets (11 int64 -> 256 B), then at most ceil(1000/64) + 10 chunks of cards per head
+    assert L.kda_varlen_workspace_size(ctypes.byref(p), 10) == 256 + (16 + 10) * 3 * 74240
+    assert L.kda_varlen_workspace_size(ctypes.byref(_p()), 10) == 0          # batch must be 1
+    assert L.kda_varlen_workspace_size(ctypes.byref(p), -1) == 0
+    ws = L.kda_varlen_workspace_size(ctypes.byref(p), 10)
+    prep = lambda pr=p, ns=10, cu=FAKE, w=FAKE, n=ws, q=FAKE: L.kda_varlen_prepare(
+        ctypes.byref(pr), ns, cu, q, FAKE, FAKE, FAKE, FAKE, w, n, None)
+    assert prep(cu=None) == 1
+    assert prep(cu=FAKE + 2) == 1       # int32 offsets need 4-byte alignment
+    assert prep(q=MISALIGNED) == 1
+    assert prep(n=ws - 1) == 3
+    assert prep(pr=_p(batch=2, seqlen=1000)) == 1
+    assert prep(pr=_p(batch=1, seqlen=1000, dk=96, dv=96)) == 2
+    assert prep(ns=0, cu=None, w=None, n=0) == 0
+    scan = lambda ns=10, cu=FAKE, g=FAKE, si=None, so=None: L.kda_varlen_scan(
+        ctypes.byref(p), ns, cu, FAKE, ws, g, si, FAKE, so, None)
+    assert scan(cu=None) == 1
+    assert scan(g=None) == 1
+    assert scan(si=MISALIGNED) == 1
+    assert scan(ns=0, cu=None) == 0
 
 
 @pytest.mark.skipif(_have_gpu(), reason="only meaningful where no HIP device exists")
