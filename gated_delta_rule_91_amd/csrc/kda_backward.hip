@@ -280,19 +280,25 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// 5. token gradients: one workgroup per chunk-head, fp32 throughout (LDS and
-// fp32 MFMA).  The value-side quantities (R, U, dO, dU) go through in
-// 16-column blocks; the products that contract over the value columns
-// accumulate in registers across the blocks.
+// 5. token gradients: one workgroup of eight waves per chunk-head, fp32
+// throughout (LDS and fp32 MFMA).  The value-side quantities (R, U, dO, dU)
+// go through in 16-column blocks; the products that contract over the value
+// columns accumulate in registers across the blocks.  Wave w works on token
+// tile w % 4; the two halves of the workgroup (w / 4) run independent
+// products side by side (R | dO and dg;  U | Ke dS + P^T dO;  dU~ | dO U^T;
+// dU~ U^T) and split the d_k-wide outputs by channel tile, so two waves share
+// each SIMD and either can issue while the other waits.
+constexpr int kGradThreads = 512;
+
 template <int DK>
 struct GradLds {
     static constexpr int C = kChunk, NB = 16;
     static constexpr int LDK = DK + 4;   // [C][DK] rows
     static constexpr int LDC = C + 4;    // [C][C] rows
     static constexpr int LDB = NB + 4;   // [C][NB] rows
+    static constexpr int LDSB = NB + 4;  // [DK][NB] rows of the staged state blocks
     static constexpr size_t K = 0;                          // k^ (zero on padded tokens)
     static constexpr size_t Q = K + (size_t)C * LDK * 4;    // q^; during the column loop, the block of S0 and dS
-    static constexpr int LDSB = NB + 4;                     // [DK][NB] rows of the staged state blocks
     static constexpr size_t EG = Q + (size_t)C * LDK * 4;   // e^gamma
     static constexpr size_t P = EG + (size_t)C * LDK * 4;   // P, then dP, then dgamma (spans P and T)
     static constexpr size_t T = P + (size_t)C * LDC * 4;    // diag(beta) A -> T, then dA
@@ -305,20 +311,22 @@ struct GradLds {
     static constexpr size_t NQ = NK + (size_t)C * 4;        // |q|
     static constexpr size_t RK = NQ + (size_t)C * 4;        // 1 / max(|k|, 1e-6)
     static constexpr size_t RQ = RK + (size_t)C * 4;        // 1 / max(|q|, 1e-6)
-    static constexpr size_t DGC = RQ + (size_t)C * 4;       // [5][DK]: per-wave sum dKe*Ke, rowsum(S0*dS)
-    static constexpr size_t BYTES = DGC + (size_t)5 * DK * 4;
+    static constexpr size_t DGC = RQ + (size_t)C * 4;       // [5][DK]: per-token-tile sum dKe*Ke, rowsum(S0*dS)
+    static constexpr size_t XD = DGC + (size_t)5 * DK * 4;  // [2 halves][k, q][C]: partial x^ . dx^
+    static constexpr size_t BYTES = XD + (size_t)4 * C * 4;
     static_assert(2 * DK * LDSB <= C * LDK, "state blocks fit over q^");
     static_assert((size_t)C * LDK <= 2 * (size_t)C * LDC, "dgamma fits over P and T");
 };
 
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardArgs a) {
     using LY = GradLds<DK>;
-    constexpr int C = kChunk, NB = LY::NB, DV = DK;
-    constexpr int LDK = LY::LDK, LDC = LY::LDC, LDB = LY::LDB;
-    constexpr int NT = DK / 16;   // channel tiles
-    constexpr int NKD = DK / 4;   // fp32 MFMA k-steps over the channels
-    constexpr int NKC = C / 4;    // ... over the tokens
+    constexpr int C = kChunk, NB = LY::NB, DV = DK, NTH = kGradThreads;
+    constexpr int LDK = LY::LDK, LDC = LY::LDC, LDB = LY::LDB, LDSB = LY::LDSB;
+    constexpr int NT = DK / 16;     // channel tiles
+    constexpr int NTH2 = NT / 2;    // ... per half
+    constexpr int NKD = DK / 4;     // fp32 MFMA k-steps over the channels
+    constexpr int NKC = C / 4;      // ... over the tokens
     constexpr float kLog2e = 1.4426950408889634f;
 
     __shared__ __attribute__((aligned(16))) char lds[LY::BYTES];
@@ -336,14 +344,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
     float* sNq = reinterpret_cast<float*>(lds + LY::NQ);
     float* sRk = reinterpret_cast<float*>(lds + LY::RK);
     float* sRq = reinterpret_cast<float*>(lds + LY::RQ);
-    float* sS0 = sQ;                       // [DK][LDSB]: S0, this block's columns
-    float* sDS = sQ + DK * LY::LDSB;       // [DK][LDSB]: dS, this block's columns
-    constexpr int LDSB = LY::LDSB;
     float* sDGC = reinterpret_cast<float*>(lds + LY::DGC);
+    float* sXD = reinterpret_cast<float*>(lds + LY::XD);
     float* sDG = sP;
+    float* sS0 = sQ;                   // [DK][LDSB]: S0, this block's columns
+    float* sDS = sQ + DK * LDSB;       // [DK][LDSB]: dS, this block's columns
 
     const int t = threadIdx.x, lane = t & 63, g = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int w4 = w & 3, half = w >> 2;   // token tile; which half of the workgroup
+    const int ct0 = half * NTH2;           // this wave's first channel tile
     const int H = a.H, NC = a.NC;
     const int64_t T = a.T;
     const int64_t wg = blockIdx.x;
@@ -365,8 +375,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
 
     // ---- 1: norms, k^, q^, e^gamma, beta ----
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-        const int i = 16 * w + ii;
+    for (int ii = 0; ii < C / 8; ++ii) {   // wave w: tokens 8w .. 8w+7
+        const int i = (C / 8) * w + ii;
         const size_t r = rowi(i);
         float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -388,18 +398,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         }
     }
     if (t < C) sBeta[t] = t < nvalid ? a.beta[rowi(t)] : 0.f;
-    for (int idx = t; idx < C * LDC; idx += kThreads) sT[idx] = 0.f;   // T's upper tiles stay zero
+    for (int idx = t; idx < C * LDC; idx += NTH) sT[idx] = 0.f;   // T's upper tiles stay zero
     __syncthreads();
     // q^ (zero on padded tokens), four channels per item
     auto load_qhat = [&]() {
-        for (int idx = t; idx < C * DK / 4; idx += kThreads) {
+        for (int idx = t; idx < C * DK / 4; idx += NTH) {
             const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
             const f32x4 x = ld4(qp + rowi(i) * DK + ch);
             st4(sQ + i * LDK + ch, i < nvalid ? x * sRq[i] : f32x4{0.f, 0.f, 0.f, 0.f});
         }
     };
     load_qhat();
-    for (int idx = t; idx < C * DK / 4; idx += kThreads) {
+    for (int idx = t; idx < C * DK / 4; idx += NTH) {
         const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
         const size_t r = rowi(i) * DK + ch;
         const bool ok = i < nvalid;
@@ -427,35 +437,43 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
     auto Qt = [&](int i, int ch) { return sQ[i * LDK + ch] * sEG[i * LDK + ch]; };
     auto Ke = [&](int i, int ch) { return Kh(i, ch) * sEG[(C - 1) * LDK + ch]; };
 
-    // ---- 2: diag(beta) A -> sT (strictly lower), P -> sP ----
+    // ---- 2: half 0: A = Kt Kh^T (kept in registers, strictly lower) and
+    // diag(beta) A -> sT; half 1: P = Qt Kh^T -> sP ----
+    f32x4 As[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if (j <= w) {
-            f32x4 xa = {0.f, 0.f, 0.f, 0.f}, xp = {0.f, 0.f, 0.f, 0.f};
+        As[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j <= w4) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (half == 0) {
 #pragma unroll 8
-            for (int s = 0; s < NKD; ++s) {
-                const float kh = Kh(16 * j + n, 4 * s + g);
-                xa = mma_f32(Kt(16 * w + n, 4 * s + g), kh, xa);
-                xp = mma_f32(Qt(16 * w + n, 4 * s + g), kh, xp);
+                for (int s = 0; s < NKD; ++s) x = mma_f32(Kt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
+            } else {
+#pragma unroll 8
+                for (int s = 0; s < NKD; ++s) x = mma_f32(Qt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * g + e, jj = 16 * j + n;
-                sT[i * LDC + jj] = jj < i ? sBeta[i] * xa[e] : 0.f;
-                sP[i * LDC + jj] = jj <= i ? xp[e] : 0.f;
+                const int i = 16 * w4 + 4 * g + e, jj = 16 * j + n;
+                if (half == 0) {
+                    As[j][e] = jj < i ? x[e] : 0.f;
+                    sT[i * LDC + jj] = jj < i ? sBeta[i] * x[e] : 0.f;
+                } else {
+                    sP[i * LDC + jj] = jj <= i ? x[e] : 0.f;
+                }
             }
-        } else {
+        } else if (half == 1) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sP[(16 * w + 4 * g + e) * LDC + 16 * j + n] = 0.f;
+            for (int e = 0; e < 4; ++e) sP[(16 * w4 + 4 * g + e) * LDC + 16 * j + n] = 0.f;
         }
     }
     __syncthreads();
 
-    // ---- 3: T = (I + diag(beta) A)^-1 in place (blocked substitution) ----
-    {   // diagonal 16x16 blocks by forward substitution; lane n of wave w owns column n of block w
+    // ---- 3: T = (I + diag(beta) A)^-1 in place (blocked substitution, half 0) ----
+    {   // diagonal 16x16 blocks by forward substitution; lane n of wave w4 owns column n of block w4
         float x[16];
-        if (g == 0) {
-            const float* Ab = sT + (16 * w) * LDC + 16 * w;
+        if (half == 0 && g == 0) {
+            const float* Ab = sT + (16 * w4) * LDC + 16 * w4;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float s = (i == n) ? 1.f : 0.f;
@@ -465,17 +483,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
             }
         }
         __syncthreads();
-        if (g == 0) {
+        if (half == 0 && g == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sT[(16 * w + i) * LDC + 16 * w + n] = x[i];
+            for (int i = 0; i < 16; ++i) sT[(16 * w4 + i) * LDC + 16 * w4 + n] = x[i];
         }
         __syncthreads();
     }
 #pragma unroll
     for (int i = 1; i < 4; ++i) {   // block row i: T_ij = -D_i sum_{kb=j}^{i-1} A_{i,kb} T_{kb,j}, wave j
         f32x4 tij = {0.f, 0.f, 0.f, 0.f};
-        if (w < i) {
-            const int j = w;
+        if (half == 0 && w4 < i) {
+            const int j = w4;
             f32x4 xx = {0.f, 0.f, 0.f, 0.f};
             for (int kb = j; kb < i; ++kb) {
 #pragma unroll
@@ -489,9 +507,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
             for (int s = 0; s < 4; ++s) tij = mma_f32(sT[(16 * i + n) * LDC + 16 * i + 4 * g + s], xx[s], tij);
         }
         __syncthreads();
-        if (w < i) {
+        if (half == 0 && w4 < i) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * g + e) * LDC + 16 * w + n] = -tij[e];
+            for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * g + e) * LDC + 16 * w4 + n] = -tij[e];
         }
         __syncthreads();
     }
@@ -503,13 +521,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
     const E* dop = reinterpret_cast<const E*>(a.d_out);
     E* dvp = reinterpret_cast<E*>(a.dv);
     E* dgp = reinterpret_cast<E*>(a.dg);
-    f32x4 dQt[NT], dKt[NT], dKe[NT], dMa[4], dPa[4];
+    // channel tiles ct0 .. ct0 + NTH2 - 1: dQt, dKt, dKe (then dKh in phase 6)
+    f32x4 aQ[NTH2], aK[NTH2], aE[NTH2], dMP[4];   // dMP: dM tiles (half 0) or dP tiles (half 1), (w4, j)
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) dQt[ct] = dKt[ct] = dKe[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c2 = 0; c2 < NTH2; ++c2) aQ[c2] = aK[c2] = aE[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dMa[j] = dPa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) dMP[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 dbp = {0.f, 0.f, 0.f, 0.f};
-    constexpr int NSI = (DK * NB / 4 + kThreads - 1) / kThreads;   // staged 4-float pieces per thread
+    constexpr int NSI = (DK * NB / 4 + NTH - 1) / NTH;   // staged 4-float pieces per thread
     float rowp[NSI];   // rowsum(S0 * dS) over the blocks so far, row (idx / 4) of piece idx
 #pragma unroll
     for (int j = 0; j < NSI; ++j) rowp[j] = 0.f;
@@ -518,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         // S0 and dS, this block's columns, to LDS (q^ is reloaded after the loop)
 #pragma unroll
         for (int j = 0; j < NSI; ++j) {
-            const int idx = t + j * kThreads;
+            const int idx = t + j * NTH;
             if (idx < DK * NB / 4) {
                 const int row = idx / (NB / 4), c4 = (idx % (NB / 4)) * 4;
                 const f32x4 x = *reinterpret_cast<const f32x4*>(S0 + (size_t)row * DV + col0 + c4);
@@ -529,79 +548,94 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
             }
         }
         __syncthreads();
-        // R = V - Kt S0 (rows 16w.., this block's columns)
-        f32x4 r;
+        if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
+            f32x4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * w + 4 * g + e;
-            r[e] = i < nvalid ? to_f32(vp[rowi(i) * DV + col0 + n]) : 0.f;
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w4 + 4 * g + e;
+                r[e] = i < nvalid ? to_f32(vp[rowi(i) * DV + col0 + n]) : 0.f;
+            }
+#pragma unroll 8
+            for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w4 + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
 #pragma unroll
-        for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
-        // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g))
+            for (int e = 0; e < 4; ++e) sR[(16 * w4 + 4 * g + e) * LDB + n] = r[e];
+        } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g))
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * w + 4 * g + e;
-            const size_t ri = rowi(i) * DV + col0 + n;
-            const float dy = dop ? to_f32(dop[ri]) : 0.f;
-            const float sg = sigmoidf_(to_f32(gp[ri]));
-            sR[i * LDB + n] = r[e];
-            sDO[i * LDB + n] = i < nvalid ? dy * sg : 0.f;
-            if (i < nvalid) dgp[ri] = from_f32<E>(dy * to_f32(op[ri]) * (1.f - sg));
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w4 + 4 * g + e;
+                const size_t ri = rowi(i) * DV + col0 + n;
+                const float dy = dop ? to_f32(dop[ri]) : 0.f;
+                const float sg = sigmoidf_(to_f32(gp[ri]));
+                sDO[i * LDB + n] = i < nvalid ? dy * sg : 0.f;
+                if (i < nvalid) dgp[ri] = from_f32<E>(dy * to_f32(op[ri]) * (1.f - sg));
+            }
         }
         __syncthreads();
-        // U = T diag(beta) R (T lower triangular)
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < 4 * (w + 1); ++s)
-            u = mma_f32(sT[(16 * w + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
+        if (half == 0) {   // U = T diag(beta) R (T lower triangular)
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4 * (w4 + 1); ++s)
+                u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sU[(16 * w + 4 * g + e) * LDB + n] = u[e];
-        // dU = Ke dS + P^T dO (P^T upper triangular)
-        f32x4 du = {0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
+        } else {           // dU = Ke dS + P^T dO (P^T upper triangular)
+            f32x4 du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
+            for (int s = 4 * w4; s < NKC; ++s)
+                du = mma_f32(sP[(4 * s + g) * LDC + 16 * w4 + n], sDO[(4 * s + g) * LDB + n], du);
 #pragma unroll
-        for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
-        for (int s = 4 * w; s < NKC; ++s) du = mma_f32(sP[(4 * s + g) * LDC + 16 * w + n], sDO[(4 * s + g) * LDB + n], du);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sDU[(16 * w + 4 * g + e) * LDB + n] = du[e];
+            for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = du[e];
+        }
         __syncthreads();
-        // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
         f32x4 dut = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 4 * w; s < NKC; ++s) dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w + n], sDU[(4 * s + g) * LDB + n], dut);
+        if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
+            for (int s = 4 * w4; s < NKC; ++s)
+                dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w4 + n], sDU[(4 * s + g) * LDB + n], dut);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * w + 4 * g + e;
-            if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
-            dbp[e] += dut[e] * sR[i * LDB + n];
-        }
-        __syncthreads();
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w4 + 4 * g + e;
+                if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
+                dbp[e] += dut[e] * sR[i * LDB + n];
+            }
+        } else {           // dP += dO U^T (column tiles j <= w4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sDU[(16 * w + 4 * g + e) * LDB + n] = dut[e];
-        __syncthreads();
-        // dM -= dU~ U^T, dP += dO U^T (column tiles j <= w)
+            for (int j = 0; j < 4; ++j) {
+                if (j <= w4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j <= w) {
-#pragma unroll
-                for (int s = 0; s < NB / 4; ++s) {
-                    const float ub = sU[(16 * j + n) * LDB + 4 * s + g];
-                    dMa[j] = mma_f32(-sDU[(16 * w + n) * LDB + 4 * s + g], ub, dMa[j]);
-                    dPa[j] = mma_f32(sDO[(16 * w + n) * LDB + 4 * s + g], ub, dPa[j]);
+                    for (int s = 0; s < NB / 4; ++s)
+                        dMP[j] = mma_f32(sDO[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g], dMP[j]);
                 }
             }
         }
-        // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T
+        __syncthreads();
+        if (half == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = dut[e];
+        }
+        __syncthreads();
+        if (half == 0) {   // dM -= dU~ U^T (column tiles j <= w4)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j <= w4) {
+#pragma unroll
+                    for (int s = 0; s < NB / 4; ++s)
+                        dMP[j] = mma_f32(-sDU[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g], dMP[j]);
+                }
+            }
+        }
+        // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles)
 #pragma unroll
         for (int s = 0; s < NB / 4; ++s) {
-            const float ao = sDO[(16 * w + n) * LDB + 4 * s + g];
-            const float ar = -sBeta[16 * w + n] * sDU[(16 * w + n) * LDB + 4 * s + g];
-            const float au = sU[(16 * w + n) * LDB + 4 * s + g];
+            const float ao = sDO[(16 * w4 + n) * LDB + 4 * s + g];
+            const float ar = -sBeta[16 * w4 + n] * sDU[(16 * w4 + n) * LDB + 4 * s + g];
+            const float au = sU[(16 * w4 + n) * LDB + 4 * s + g];
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const int si = (16 * ct + n) * LDSB + 4 * s + g;
+            for (int c2 = 0; c2 < NTH2; ++c2) {
+                const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * s + g;
                 const float b0 = sS0[si], b1 = sDS[si];
-                dQt[ct] = mma_f32(ao, b0, dQt[ct]);
-                dKt[ct] = mma_f32(ar, b0, dKt[ct]);
-                dKe[ct] = mma_f32(au, b1, dKe[ct]);
+                aQ[c2] = mma_f32(ao, b0, aQ[c2]);
+                aK[c2] = mma_f32(ar, b0, aK[c2]);
+                aE[c2] = mma_f32(au, b1, aE[c2]);
             }
         }
         __syncthreads();
@@ -613,25 +647,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         float x = rowp[j];
         x += __shfl_xor(x, 1);
         x += __shfl_xor(x, 2);
-        const int idx = t + j * kThreads;
+        const int idx = t + j * NTH;
         if (idx < DK * NB / 4 && (idx & 3) == 0) sDGC[4 * DK + idx / (NB / 4)] = x;
     }
     load_qhat();
 
-    // ---- 5: dbeta; dA and dP to LDS ----
-    {
+    // ---- 5: dbeta, dA -> sT (half 0); dP -> sP (half 1) ----
+    if (half == 0) {
         f32x4 db = dbp;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j <= w) {   // A tile (w, j) again, for sum_j dM_ij A_ij
-                f32x4 xa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-                for (int s = 0; s < NKD; ++s) xa = mma_f32(Kt(16 * w + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), xa);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (16 * j + n < 16 * w + 4 * g + e) db[e] += dMa[j][e] * xa[e];
-            }
-        }
+            for (int e = 0; e < 4; ++e) db[e] += dMP[j][e] * As[j][e];   // As: strictly lower, zero for j > w4
 #pragma unroll
         for (int m = 1; m < 16; m <<= 1)
 #pragma unroll
@@ -639,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         if (n == 0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * g + e;
+                const int i = 16 * w4 + 4 * g + e;
                 if (i < nvalid) a.dbeta[rowi(i)] = db[e];
             }
         }
@@ -648,66 +675,67 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 16 * w + 4 * g + e, jj = 16 * j + n;
-            sT[i * LDC + jj] = (j <= w && jj < i) ? sBeta[i] * dMa[j][e] : 0.f;   // dA
-            sP[i * LDC + jj] = (j <= w && jj <= i) ? dPa[j][e] : 0.f;            // dP
+            const int i = 16 * w4 + 4 * g + e, jj = 16 * j + n;
+            if (half == 0) sT[i * LDC + jj] = (j <= w4 && jj < i) ? sBeta[i] * dMP[j][e] : 0.f;   // dA
+            else sP[i * LDC + jj] = (j <= w4 && jj <= i) ? dMP[j][e] : 0.f;                      // dP
         }
     __syncthreads();
 
     // ---- 6: dQt += dP Kh, dKt += dA Kh, dKh = dP^T Qt + dA^T Kt ----
-    f32x4 dKh[NT];
+    f32x4 aH[NTH2];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) dKh[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < 4 * (w + 1); ++s) {
-        const float ap = sP[(16 * w + n) * LDC + 4 * s + g], aa = sT[(16 * w + n) * LDC + 4 * s + g];
+    for (int c2 = 0; c2 < NTH2; ++c2) aH[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4 * (w4 + 1); ++s) {
+        const float ap = sP[(16 * w4 + n) * LDC + 4 * s + g], aa = sT[(16 * w4 + n) * LDC + 4 * s + g];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            const float kh = Kh(4 * s + g, 16 * ct + n);
-            dQt[ct] = mma_f32(ap, kh, dQt[ct]);
-            dKt[ct] = mma_f32(aa, kh, dKt[ct]);
+        for (int c2 = 0; c2 < NTH2; ++c2) {
+            const float kh = Kh(4 * s + g, 16 * (ct0 + c2) + n);
+            aQ[c2] = mma_f32(ap, kh, aQ[c2]);
+            aK[c2] = mma_f32(aa, kh, aK[c2]);
         }
     }
-    for (int s = 4 * w; s < NKC; ++s) {
-        const float ap = sP[(4 * s + g) * LDC + 16 * w + n], aa = sT[(4 * s + g) * LDC + 16 * w + n];
+    for (int s = 4 * w4; s < NKC; ++s) {
+        const float ap = sP[(4 * s + g) * LDC + 16 * w4 + n], aa = sT[(4 * s + g) * LDC + 16 * w4 + n];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            dKh[ct] = mma_f32(ap, Qt(4 * s + g, 16 * ct + n), dKh[ct]);
-            dKh[ct] = mma_f32(aa, Kt(4 * s + g, 16 * ct + n), dKh[ct]);
+        for (int c2 = 0; c2 < NTH2; ++c2) {
+            const int ch = 16 * (ct0 + c2) + n;
+            aH[c2] = mma_f32(ap, Qt(4 * s + g, ch), aH[c2]);
+            aH[c2] = mma_f32(aa, Kt(4 * s + g, ch), aH[c2]);
         }
     }
 
-    // ---- 7: through the decay folding: dq^, dk^, dgamma (in place) ----
+    // ---- 7: through the decay folding: dq^ (aQ), dk^ (aK), dgamma (aH), in place ----
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-        const int ch = 16 * ct + n;
+    for (int c2 = 0; c2 < NTH2; ++c2) {
+        const int ch = 16 * (ct0 + c2) + n;
         const float egc = sEG[(C - 1) * LDK + ch];
         float gsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 16 * w + 4 * g + e;
+            const int i = 16 * w4 + 4 * g + e;
             const float kh = sK[i * LDK + ch], qh = sQ[i * LDK + ch], eg = sEG[i * LDK + ch];
             const float ieg = __builtin_amdgcn_rcpf(eg);
             const float ktv = kh * eg, khv = kh * ieg, qtv = qh * eg, kev = khv * egc;
-            const float dqt = dQt[ct][e], dkt = dKt[ct][e], dkhv = dKh[ct][e], dke = dKe[ct][e];
-            dQt[ct][e] = dqt * eg;                                          // dq^
-            dKt[ct][e] = dkt * eg + dkhv * ieg + dke * egc * ieg;           // dk^
-            dKh[ct][e] = dkt * ktv - dkhv * khv + dqt * qtv - dke * kev;    // dgamma
+            const float dqt = aQ[c2][e], dkt = aK[c2][e], dkhv = aH[c2][e], dke = aE[c2][e];
+            aQ[c2][e] = dqt * eg;                                           // dq^
+            aK[c2][e] = dkt * eg + dkhv * ieg + dke * egc * ieg;            // dk^
+            aH[c2][e] = dkt * ktv - dkhv * khv + dqt * qtv - dke * kev;     // dgamma
             gsum += dke * kev;
         }
         gsum += __shfl_xor(gsum, 16);
         gsum += __shfl_xor(gsum, 32);
-        if (g == 0) sDGC[w * DK + ch] = gsum;
+        if (g == 0) sDGC[w4 * DK + ch] = gsum;
     }
     // ---- 8: L2 normalisation: dx = (dx^ - x^ (x^ . dx^)) / |x| (constant divisor below 1e-6) ----
     {
         f32x4 kd = {0.f, 0.f, 0.f, 0.f}, qd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
+        for (int c2 = 0; c2 < NTH2; ++c2)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * g + e, ch = 16 * ct + n;
-                kd[e] += sK[i * LDK + ch] * dKt[ct][e];
-                qd[e] += sQ[i * LDK + ch] * dQt[ct][e];
+                const int i = 16 * w4 + 4 * g + e, ch = 16 * (ct0 + c2) + n;
+                kd[e] += sK[i * LDK + ch] * aK[c2][e];
+                qd[e] += sQ[i * LDK + ch] * aQ[c2][e];
             }
 #pragma unroll
         for (int m = 1; m < 16; m <<= 1)
@@ -716,32 +744,39 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
                 kd[e] += __shfl_xor(kd[e], m);
                 qd[e] += __shfl_xor(qd[e], m);
             }
+        if (n == 0) {   // this half's share of the per-token dot products
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sXD[(2 * half) * C + 16 * w4 + 4 * g + e] = kd[e];
+                sXD[(2 * half + 1) * C + 16 * w4 + 4 * g + e] = qd[e];
+            }
+        }
+        __syncthreads();
         E* dkp = reinterpret_cast<E*>(a.dk);
         E* dqp = reinterpret_cast<E*>(a.dq);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 16 * w + 4 * g + e;
+            const int i = 16 * w4 + 4 * g + e;
             if (i < nvalid) {
                 const float nk = sNk[i], nq = sNq[i];
+                const float kdi = sXD[i] + sXD[2 * C + i], qdi = sXD[C + i] + sXD[3 * C + i];
                 const size_t ri = rowi(i) * DK;
 #pragma unroll
-                for (int ct = 0; ct < NT; ++ct) {
-                    const int ch = 16 * ct + n;
-                    const float dkx = nk < 1e-6f ? dKt[ct][e] * 1e6f : (dKt[ct][e] - sK[i * LDK + ch] * kd[e]) / nk;
-                    const float dqx = nq < 1e-6f ? dQt[ct][e] * 1e6f : (dQt[ct][e] - sQ[i * LDK + ch] * qd[e]) / nq;
+                for (int c2 = 0; c2 < NTH2; ++c2) {
+                    const int ch = 16 * (ct0 + c2) + n;
+                    const float dkx = nk < 1e-6f ? aK[c2][e] * 1e6f : (aK[c2][e] - sK[i * LDK + ch] * kdi) / nk;
+                    const float dqx = nq < 1e-6f ? aQ[c2][e] * 1e6f : (aQ[c2][e] - sQ[i * LDK + ch] * qdi) / nq;
                     dkp[ri + ch] = from_f32<E>(dkx);
                     dqp[ri + ch] = from_f32<E>(dqx);
                 }
             }
         }
     }
-    // ---- 9: dgamma to LDS (over dP and dA) ----
-    __syncthreads();
+    // ---- 9: dgamma to LDS (over dP and dA, read for the last time in phase 6) ----
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
+    for (int c2 = 0; c2 < NTH2; ++c2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sDG[(16 * w + 4 * g + e) * LDK + 16 * ct + n] = dKh[ct][e];
-
+        for (int e = 0; e < 4; ++e) sDG[(16 * w4 + 4 * g + e) * LDK + 16 * (ct0 + c2) + n] = aH[c2][e];
     __syncthreads();
     // ---- 10: dlog_alpha = reverse cumulative sum of dgamma (zero where the floor binds) ----
     if (t < DK) {   // in place, channel t
@@ -753,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_bwd_grad_kernel(BackwardArgs 
         }
     }
     __syncthreads();
-    for (int idx = t; idx < nvalid * (DK / 4); idx += kThreads) {
+    for (int idx = t; idx < nvalid * (DK / 4); idx += NTH) {
         const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
         const size_t r = rowi(i) * DK + ch;
         const f32x4 la = *reinterpret_cast<const f32x4*>(a.log_alpha + r);
@@ -780,7 +815,7 @@ hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
                        a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || chunks == 0) return e;
-    hipLaunchKernelGGL((kda_bwd_grad_kernel<E, DK>), dim3((unsigned)chunks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((kda_bwd_grad_kernel<E, DK>), dim3((unsigned)chunks), dim3(kGradThreads), 0, s, a);
     return hipGetLastError();
 }
 
