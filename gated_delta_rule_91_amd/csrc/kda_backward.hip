@@ -229,44 +229,72 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
 
     const char* bcards = a.ws + L.bcards + (size_t)bh * NC * BC::BYTES;
     float* dstates = reinterpret_cast<float*>(a.ws + L.dstates) + (size_t)bh * NC * DK * DV + col0 + n;
-    for (int c = NC - 1; c >= 0; --c) {
-        const char* bc = bcards + (size_t)c * BC::BYTES;
+    // one chunk's operands in registers: a two-slot ring loads chunk c - 1
+    // while chunk c computes (loads are unconditional: past chunk 0 the ring
+    // re-reads chunk 0)
+    struct Ops {
+        F kea[NKD], qtt[MTS][NKC], wkt[MTS][NKC], dot[NKC];
+        f32x4 gv[MTS];
+        f32x4 dul;
+    };
+    auto load = [&](Ops& o, int c) {
+        const char* bc = bcards + (size_t)(c > 0 ? c : 0) * BC::BYTES;
+        o.dul = ld4(reinterpret_cast<const E*>(bc + BC::DUL) + ((size_t)(tile * 4 + w) * 64 + lane) * 4);
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) o.kea[s] = *reinterpret_cast<const F*>(bc + BC::KEA + (w * NKD + s) * KSB + lane * FB);
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) o.dot[s] = *reinterpret_cast<const F*>(bc + BC::DOT + (tile * NKC + s) * KSB + lane * FB);
+#pragma unroll
+        for (int mt = 0; mt < MTS; ++mt) {
+            const int rb = (DK / 64) * w + mt;
+            o.gv[mt] = *reinterpret_cast<const f32x4*>(bc + BC::G + ((DK / 4) * w + 16 * mt + 4 * g) * 4);
+#pragma unroll
+            for (int s = 0; s < NKC; ++s) {
+                o.qtt[mt][s] = *reinterpret_cast<const F*>(bc + BC::QTT + (rb * NKC + s) * KSB + lane * FB);
+                o.wkt[mt][s] = *reinterpret_cast<const F*>(bc + BC::WKT + (rb * NKC + s) * KSB + lane * FB);
+            }
+        }
+    };
+    auto step = [&](const Ops& o, int c) {
         float* dst = dstates + (size_t)c * DK * DV;   // gradient of the state leaving chunk c
 #pragma unroll
         for (int mt = 0; mt < MTS; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[(size_t)((DK / 4) * w + 16 * mt + 4 * g + e) * DV] = dS[mt][e];
         // dU rows 16w..16w+15 = P^T dO + Ke dS
-        f32x4 du = ld4(reinterpret_cast<const E*>(bc + BC::DUL) + ((size_t)(tile * 4 + w) * 64 + lane) * 4);
+        f32x4 du = o.dul;
 #pragma unroll
-        for (int s = 0; s < NKD; ++s)
-            du = M::mma(*reinterpret_cast<const F*>(bc + BC::KEA + (w * NKD + s) * KSB + lane * FB),
-                        ld_frag(sS, LDS_S, n, s * KS, g), du);
+        for (int s = 0; s < NKD; ++s) du = M::mma(o.kea[s], ld_frag(sS, LDS_S, n, s * KS, g), du);
         st4(sU + n * LDS_U + 16 * w + 4 * g, du);
         __syncthreads();
         // dS <- G dS + Qt^T dO - Wk^T dU
-        F ub[NKC], ob[NKC];
+        F ub[NKC];
 #pragma unroll
-        for (int s = 0; s < NKC; ++s) {
-            ub[s] = ld_frag(sU, LDS_U, n, s * KS, g);
-            ob[s] = *reinterpret_cast<const F*>(bc + BC::DOT + (tile * NKC + s) * KSB + lane * FB);
-        }
+        for (int s = 0; s < NKC; ++s) ub[s] = ld_frag(sU, LDS_U, n, s * KS, g);
 #pragma unroll
         for (int mt = 0; mt < MTS; ++mt) {
-            const int rb = (DK / 64) * w + mt;
-            const f32x4 gv = *reinterpret_cast<const f32x4*>(bc + BC::G + ((DK / 4) * w + 16 * mt + 4 * g) * 4);
-            f32x4 acc = dS[mt] * gv;
+            f32x4 acc = dS[mt] * o.gv[mt];
 #pragma unroll
-            for (int s = 0; s < NKC; ++s)
-                acc = M::mma(*reinterpret_cast<const F*>(bc + BC::QTT + (rb * NKC + s) * KSB + lane * FB), ob[s], acc);
+            for (int s = 0; s < NKC; ++s) acc = M::mma(o.qtt[mt][s], o.dot[s], acc);
 #pragma unroll
-            for (int s = 0; s < NKC; ++s)
-                acc = M::mma(*reinterpret_cast<const F*>(bc + BC::WKT + (rb * NKC + s) * KSB + lane * FB), ub[s], acc);
+            for (int s = 0; s < NKC; ++s) acc = M::mma(o.wkt[mt][s], ub[s], acc);
             dS[mt] = acc;
         }
 #pragma unroll
         for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, dS[mt]);
         __syncthreads();
+    };
+    if (NC > 0) {
+        Ops o0, o1;
+        load(o0, NC - 1);
+        int c = NC - 1;
+        for (; c >= 1; c -= 2) {
+            load(o1, c - 1);
+            step(o0, c);
+            load(o0, c - 2);
+            step(o1, c - 1);
+        }
+        if (c == 0) step(o0, 0);
     }
     if (a.d_state_in) {
 #pragma unroll
