@@ -46,6 +46,18 @@ constexpr int kXcds = 8;
 __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// bf16 16x16x16: lane (n, g) supplies A[n][4g..4g+3] and B[4g..4g+3][n]
+__device__ __forceinline__ f32x4 mma_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+    return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+__device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 rcp4(f32x4 x) {
+    return f32x4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
+                 __builtin_amdgcn_rcpf(x[3])};
+}
 
 // The operands of the reverse hand-off for one (batch row, head, chunk):
 //   KEA [C x DK]  Ke in A-fragment order          (dU = Ke dS + ...)
@@ -315,7 +327,11 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
 // tile w % 4; the two halves of the workgroup (w / 4) run independent
 // products side by side (R | dO and dg;  U | Ke dS + P^T dO;  dU~ | dO U^T;
 // dU~ U^T) and split the d_k-wide outputs by channel tile, so two waves share
-// each SIMD and either can issue while the other waits.
+// each SIMD and either can issue while the other waits.  With bf16 I/O the
+// Gram matrices, R, Ke dS and the three products that contract over the value
+// columns take bf16 operands (16x16x16 MFMA, fp32 accumulation), the operand
+// precision of the forward cards; everything else, and all of fp32 I/O, stays
+// on fp32 MFMA.
 constexpr int kGradThreads = 512;
 
 template <int DK>
@@ -356,6 +372,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     constexpr int NKD = DK / 4;     // fp32 MFMA k-steps over the channels
     constexpr int NKC = C / 4;      // ... over the tokens
     constexpr float kLog2e = 1.4426950408889634f;
+    constexpr bool BF = sizeof(E) == 2;   // bf16 operands for the big products
 
     __shared__ __attribute__((aligned(16))) char lds[LY::BYTES];
     float* sK = reinterpret_cast<float*>(lds + LY::K);
@@ -374,6 +391,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     float* sRq = reinterpret_cast<float*>(lds + LY::RQ);
     float* sDGC = reinterpret_cast<float*>(lds + LY::DGC);
     float* sXD = reinterpret_cast<float*>(lds + LY::XD);
+    static_assert(LDK % 4 == 0 && LDB % 4 == 0 && LY::LDSB % 4 == 0, "16-byte rows for the bf16 operand reads");
     float* sDG = sP;
     float* sS0 = sQ;                   // [DK][LDSB]: S0, this block's columns
     float* sDS = sQ + DK * LDSB;       // [DK][LDSB]: dS, this block's columns
@@ -473,7 +491,17 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         As[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (j <= w4) {
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (half == 0) {
+            if constexpr (BF) {   // rows of Kt (or Qt) against rows of Kh, 16 channels per step
+                const float* xa = (half == 0 ? sK : sQ) + (16 * w4 + n) * LDK;
+                const float* ea = sEG + (16 * w4 + n) * LDK;
+                const float* kb = sK + (16 * j + n) * LDK;
+                const float* eb = sEG + (16 * j + n) * LDK;
+#pragma unroll 4
+                for (int s = 0; s < DK / 16; ++s) {
+                    const int c0 = 16 * s + 4 * g;
+                    x = mma_bf16(to_bf16x4(ld4s(xa + c0) * ld4s(ea + c0)), to_bf16x4(ld4s(kb + c0) * rcp4(ld4s(eb + c0))), x);
+                }
+            } else if (half == 0) {
 #pragma unroll 8
                 for (int s = 0; s < NKD; ++s) x = mma_f32(Kt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
             } else {
@@ -583,8 +611,20 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 const int i = 16 * w4 + 4 * g + e;
                 r[e] = i < nvalid ? to_f32(vp[rowi(i) * DV + col0 + n]) : 0.f;
             }
+            if constexpr (BF) {
+                const float* xa = sK + (16 * w4 + n) * LDK;
+                const float* ea = sEG + (16 * w4 + n) * LDK;
+#pragma unroll 4
+                for (int s = 0; s < DK / 16; ++s) {
+                    const int c0 = 16 * s + 4 * g;
+                    const f32x4 bs = {sS0[c0 * LDSB + n], sS0[(c0 + 1) * LDSB + n], sS0[(c0 + 2) * LDSB + n],
+                                      sS0[(c0 + 3) * LDSB + n]};
+                    r = mma_bf16(to_bf16x4(-(ld4s(xa + c0) * ld4s(ea + c0))), to_bf16x4(bs), r);
+                }
+            } else {
 #pragma unroll 8
-            for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w4 + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
+                for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w4 + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) sR[(16 * w4 + 4 * g + e) * LDB + n] = r[e];
         } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g))
@@ -607,8 +647,21 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
         } else {           // dU = Ke dS + P^T dO (P^T upper triangular)
             f32x4 du = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BF) {
+                const float* xa = sK + (16 * w4 + n) * LDK;
+                const float* ea = sEG + (16 * w4 + n) * LDK;
+                const float* ec = sEG + (C - 1) * LDK;
+#pragma unroll 4
+                for (int s = 0; s < DK / 16; ++s) {
+                    const int c0 = 16 * s + 4 * g;
+                    const f32x4 bs = {sDS[c0 * LDSB + n], sDS[(c0 + 1) * LDSB + n], sDS[(c0 + 2) * LDSB + n],
+                                      sDS[(c0 + 3) * LDSB + n]};
+                    du = mma_bf16(to_bf16x4(ld4s(xa + c0) * rcp4(ld4s(ea + c0)) * ld4s(ec + c0)), to_bf16x4(bs), du);
+                }
+            } else {
 #pragma unroll 8
-            for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
+                for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
+            }
             for (int s = 4 * w4; s < NKC; ++s)
                 du = mma_f32(sP[(4 * s + g) * LDC + 16 * w4 + n], sDO[(4 * s + g) * LDB + n], du);
 #pragma unroll
@@ -652,6 +705,20 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             }
         }
         // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles)
+        if constexpr (BF) {   // the block's 16 value columns are one bf16 k-step
+            const int ra = (16 * w4 + n) * LDB + 4 * g;
+            const bf16x4 ao = to_bf16x4(ld4s(sDO + ra));
+            const bf16x4 ar = to_bf16x4(-sBeta[16 * w4 + n] * ld4s(sDU + ra));
+            const bf16x4 au = to_bf16x4(ld4s(sU + ra));
+#pragma unroll
+            for (int c2 = 0; c2 < NTH2; ++c2) {
+                const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * g;
+                const bf16x4 b0 = to_bf16x4(ld4s(sS0 + si)), b1 = to_bf16x4(ld4s(sDS + si));
+                aQ[c2] = mma_bf16(ao, b0, aQ[c2]);
+                aK[c2] = mma_bf16(ar, b0, aK[c2]);
+                aE[c2] = mma_bf16(au, b1, aE[c2]);
+            }
+        } else
 #pragma unroll
         for (int s = 0; s < NB / 4; ++s) {
             const float ao = sDO[(16 * w4 + n) * LDB + 4 * s + g];
