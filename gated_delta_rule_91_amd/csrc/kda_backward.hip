@@ -328,10 +328,11 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
 // products side by side (R | dO and dg;  U | Ke dS + P^T dO;  dU~ | dO U^T;
 // dU~ U^T) and split the d_k-wide outputs by channel tile, so two waves share
 // each SIMD and either can issue while the other waits.  With bf16 I/O the
-// Gram matrices, R, Ke dS and the three products that contract over the value
-// columns take bf16 operands (16x16x16 MFMA, fp32 accumulation), the operand
-// precision of the forward cards; everything else, and all of fp32 I/O, stays
-// on fp32 MFMA.
+// Gram matrices, R, U, Ke dS + P^T dO, dU~, dM, dP and the three products
+// that contract over the value columns take bf16 operands (16x16x16 MFMA,
+// fp32 accumulation), the operand precision of the forward cards; the
+// products after the column loop stay on fp32 MFMA (dgamma takes their
+// differences), as does all of fp32 I/O.
 constexpr int kGradThreads = 512;
 
 template <int DK>
@@ -641,8 +642,17 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         __syncthreads();
         if (half == 0) {   // U = T diag(beta) R (T lower triangular)
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < 4 * (w4 + 1); ++s)
-                u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
+            if constexpr (BF) {   // 16-token k-blocks 0 .. w4
+                for (int s = 0; s <= w4; ++s) {
+                    const int j0 = 16 * s + 4 * g;
+                    const f32x4 bb = {sBeta[j0] * sR[j0 * LDB + n], sBeta[j0 + 1] * sR[(j0 + 1) * LDB + n],
+                                      sBeta[j0 + 2] * sR[(j0 + 2) * LDB + n], sBeta[j0 + 3] * sR[(j0 + 3) * LDB + n]};
+                    u = mma_bf16(to_bf16x4(ld4s(sT + (16 * w4 + n) * LDC + j0)), to_bf16x4(bb), u);
+                }
+            } else {
+                for (int s = 0; s < 4 * (w4 + 1); ++s)
+                    u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
         } else {           // dU = Ke dS + P^T dO (P^T upper triangular)
@@ -662,16 +672,38 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll 8
                 for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
             }
-            for (int s = 4 * w4; s < NKC; ++s)
-                du = mma_f32(sP[(4 * s + g) * LDC + 16 * w4 + n], sDO[(4 * s + g) * LDB + n], du);
+            if constexpr (BF) {   // 16-token k-blocks w4 .. 3
+                for (int s = w4; s < 4; ++s) {
+                    const int j0 = 16 * s + 4 * g, ci = 16 * w4 + n;
+                    const f32x4 ap = {sP[j0 * LDC + ci], sP[(j0 + 1) * LDC + ci], sP[(j0 + 2) * LDC + ci],
+                                      sP[(j0 + 3) * LDC + ci]};
+                    const f32x4 bd = {sDO[j0 * LDB + n], sDO[(j0 + 1) * LDB + n], sDO[(j0 + 2) * LDB + n],
+                                      sDO[(j0 + 3) * LDB + n]};
+                    du = mma_bf16(to_bf16x4(ap), to_bf16x4(bd), du);
+                }
+            } else {
+                for (int s = 4 * w4; s < NKC; ++s)
+                    du = mma_f32(sP[(4 * s + g) * LDC + 16 * w4 + n], sDO[(4 * s + g) * LDB + n], du);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = du[e];
         }
         __syncthreads();
         f32x4 dut = {0.f, 0.f, 0.f, 0.f};
         if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
-            for (int s = 4 * w4; s < NKC; ++s)
-                dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w4 + n], sDU[(4 * s + g) * LDB + n], dut);
+            if constexpr (BF) {   // 16-token k-blocks w4 .. 3
+                for (int s = w4; s < 4; ++s) {
+                    const int j0 = 16 * s + 4 * g, ci = 16 * w4 + n;
+                    const f32x4 at = {sT[j0 * LDC + ci], sT[(j0 + 1) * LDC + ci], sT[(j0 + 2) * LDC + ci],
+                                      sT[(j0 + 3) * LDC + ci]};
+                    const f32x4 bd = {sDU[j0 * LDB + n], sDU[(j0 + 1) * LDB + n], sDU[(j0 + 2) * LDB + n],
+                                      sDU[(j0 + 3) * LDB + n]};
+                    dut = mma_bf16(to_bf16x4(at), to_bf16x4(bd), dut);
+                }
+            } else {
+                for (int s = 4 * w4; s < NKC; ++s)
+                    dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w4 + n], sDU[(4 * s + g) * LDB + n], dut);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * w4 + 4 * g + e;
@@ -679,12 +711,18 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 dbp[e] += dut[e] * sR[i * LDB + n];
             }
         } else {           // dP += dO U^T (column tiles j <= w4)
+            const bf16x4 ao = to_bf16x4(ld4s(sDO + (16 * w4 + n) * LDB + 4 * g));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (j <= w4) {
+                    if constexpr (BF) {
+                        dMP[j] = mma_bf16(ao, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
+                    } else {
 #pragma unroll
-                    for (int s = 0; s < NB / 4; ++s)
-                        dMP[j] = mma_f32(sDO[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g], dMP[j]);
+                        for (int s = 0; s < NB / 4; ++s)
+                            dMP[j] = mma_f32(sDO[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
+                                             dMP[j]);
+                    }
                 }
             }
         }
@@ -695,12 +733,18 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         }
         __syncthreads();
         if (half == 0) {   // dM -= dU~ U^T (column tiles j <= w4)
+            const bf16x4 am = to_bf16x4(-ld4s(sDU + (16 * w4 + n) * LDB + 4 * g));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (j <= w4) {
+                    if constexpr (BF) {
+                        dMP[j] = mma_bf16(am, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
+                    } else {
 #pragma unroll
-                    for (int s = 0; s < NB / 4; ++s)
-                        dMP[j] = mma_f32(-sDU[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g], dMP[j]);
+                        for (int s = 0; s < NB / 4; ++s)
+                            dMP[j] = mma_f32(-sDU[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
+                                             dMP[j]);
+                    }
                 }
             }
         }
@@ -780,22 +824,26 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     f32x4 aH[NTH2];
 #pragma unroll
     for (int c2 = 0; c2 < NTH2; ++c2) aH[c2] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < 4 * (w4 + 1); ++s) {
-        const float ap = sP[(16 * w4 + n) * LDC + 4 * s + g], aa = sT[(16 * w4 + n) * LDC + 4 * s + g];
+    // fp32 for every I/O type: dgamma takes differences of these products
+    // (dKt Kt - dKh Kh), and bf16 operands here doubled its error
+    {
+        for (int s = 0; s < 4 * (w4 + 1); ++s) {
+            const float ap = sP[(16 * w4 + n) * LDC + 4 * s + g], aa = sT[(16 * w4 + n) * LDC + 4 * s + g];
 #pragma unroll
-        for (int c2 = 0; c2 < NTH2; ++c2) {
-            const float kh = Kh(4 * s + g, 16 * (ct0 + c2) + n);
-            aQ[c2] = mma_f32(ap, kh, aQ[c2]);
-            aK[c2] = mma_f32(aa, kh, aK[c2]);
+            for (int c2 = 0; c2 < NTH2; ++c2) {
+                const float kh = Kh(4 * s + g, 16 * (ct0 + c2) + n);
+                aQ[c2] = mma_f32(ap, kh, aQ[c2]);
+                aK[c2] = mma_f32(aa, kh, aK[c2]);
+            }
         }
-    }
-    for (int s = 4 * w4; s < NKC; ++s) {
-        const float ap = sP[(4 * s + g) * LDC + 16 * w4 + n], aa = sT[(4 * s + g) * LDC + 16 * w4 + n];
+        for (int s = 4 * w4; s < NKC; ++s) {
+            const float ap = sP[(4 * s + g) * LDC + 16 * w4 + n], aa = sT[(4 * s + g) * LDC + 16 * w4 + n];
 #pragma unroll
-        for (int c2 = 0; c2 < NTH2; ++c2) {
-            const int ch = 16 * (ct0 + c2) + n;
-            aH[c2] = mma_f32(ap, Qt(4 * s + g, ch), aH[c2]);
-            aH[c2] = mma_f32(aa, Kt(4 * s + g, ch), aH[c2]);
+            for (int c2 = 0; c2 < NTH2; ++c2) {
+                const int ch = 16 * (ct0 + c2) + n;
+                aH[c2] = mma_f32(ap, Qt(4 * s + g, ch), aH[c2]);
+                aH[c2] = mma_f32(aa, Kt(4 * s + g, ch), aH[c2]);
+            }
         }
     }
 
