@@ -22,6 +22,9 @@ Also reported on the same JSON line:
   * the segmented (context-parallel) prefill of 1,048,576 tokens x 8 heads as
     16 segments: per-call times of prepare, segment summaries, in-order
     combine and the per-segment recompute;
+  * packed variable-length prefill: the long workload's 65,536 tokens x 32
+    heads re-cut into sequences of a seeded length mix (kda_varlen_prepare +
+    kda_varlen_scan), tokens/s beside the uniform step;
   * the backward pass (gradients of every prefill input and of the initial
     state) on the medium prefill workload B=4, T=4,096, H=16, d=128 bf16:
     ms per call and token-heads/s, beside the forward on the same inputs;
@@ -83,6 +86,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-segmented", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -301,6 +305,45 @@ def main():
                      "scan": SCAN_BYTES * ths / (times["scan"] * 1e-3) / 1e9},
         }
         del ds, wss, outs
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------- packed variable-length
+    if not args.no_varlen and not args.decode_only:
+        import numpy as np
+        inp = workload(2)
+        dl = kda.to_device(inp, dev)
+        # lengths: log-uniform between 64 and 8,192 tokens (seeded), the last one
+        # taking the remainder, so short and long requests mix as in serving
+        rng = np.random.default_rng(2024)
+        lens = []
+        while sum(lens) < T:
+            lens.append(int(min(T - sum(lens), round(float(np.exp(rng.uniform(np.log(64), np.log(8192))))))))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        pv = kda.problem(1, T, H, D, D, kda.KDA_BF16, inp.log_alpha_min)
+        wsv = torch.empty(kda.varlen_workspace_size(pv, len(lens)), dtype=torch.uint8, device=dev)
+        outv = torch.empty_like(dl["g"])
+
+        def vstep():
+            kda.varlen_prepare(dl["q"], dl["k"], dl["v"], dl["log_alpha"], dl["beta"], inp.log_alpha_min, cu,
+                               workspace=wsv)
+            kda.varlen_scan(wsv, dl["g"], inp.log_alpha_min, cu, out=outv, want_state=True)
+
+        vstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            vstep()
+        e1.record()
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / reps
+        log(f"[bench] varlen {vms:.3f} ms for {len(lens)} sequences ({min(lens)}..{max(lens)} tokens)")
+        result["varlen"] = {"workload": f"kda-varlen-prefill {len(lens)} sequences, {T} packed tokens, H{H} d{D} bf16",
+                            "ms": vms, "tokens_per_s": T / (vms * 1e-3), "n_seq": len(lens),
+                            "min_len": min(lens), "max_len": max(lens),
+                            "GBps": PATH_BYTES * T * H / (vms * 1e-3) / 1e9}
+        del dl, wsv, outv
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- backward
