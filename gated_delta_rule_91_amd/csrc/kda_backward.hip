@@ -589,6 +589,38 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     float rowp[NSI];   // rowsum(S0 * dS) over the blocks so far, row (idx / 4) of piece idx
 #pragma unroll
     for (int j = 0; j < NSI; ++j) rowp[j] = 0.f;
+    // the global inputs of a column block, fetched one block ahead into
+    // registers (every load unconditional: addresses are clamped, the block
+    // after the last re-reads the last)
+    struct Pre {
+        f32x4 s[NSI], d[NSI];   // S0 and dS pieces
+        f32x4 a, b, c;          // V (half 0), or d_out, g, out (half 1)
+    };
+    auto fetch = [&](int vb) {
+        Pre p;
+        const int col0 = NB * (vb < DV / NB ? vb : DV / NB - 1);
+#pragma unroll
+        for (int j = 0; j < NSI; ++j) {
+            const int idx = t + j * NTH < DK * NB / 4 ? t + j * NTH : DK * NB / 4 - 1;
+            const int row = idx / (NB / 4), c4 = (idx % (NB / 4)) * 4;
+            p.s[j] = *reinterpret_cast<const f32x4*>(S0 + (size_t)row * DV + col0 + c4);
+            p.d[j] = *reinterpret_cast<const f32x4*>(dSo + (size_t)row * DV + col0 + c4);
+        }
+        // both halves load three values per element (the V pointer twice on
+        // half 0), so no load sits under a branch
+        const E* pa = half == 0 ? vp : (dop ? dop : gp);
+        const E* pb = half == 0 ? vp : gp;
+        const E* pc = half == 0 ? vp : op;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const size_t ri = rowi(16 * w4 + 4 * g + e) * DV + col0 + n;
+            p.a[e] = (half == 0 || dop) ? to_f32(pa[ri]) : 0.f;
+            p.b[e] = to_f32(pb[ri]);
+            p.c[e] = to_f32(pc[ri]);
+        }
+        return p;
+    };
+    Pre pre = fetch(0);
     for (int vb = 0; vb < DV / NB; ++vb) {
         const int col0 = NB * vb;
         // S0 and dS, this block's columns, to LDS (q^ is reloaded after the loop)
@@ -597,21 +629,19 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             const int idx = t + j * NTH;
             if (idx < DK * NB / 4) {
                 const int row = idx / (NB / 4), c4 = (idx % (NB / 4)) * 4;
-                const f32x4 x = *reinterpret_cast<const f32x4*>(S0 + (size_t)row * DV + col0 + c4);
-                const f32x4 y = *reinterpret_cast<const f32x4*>(dSo + (size_t)row * DV + col0 + c4);
+                const f32x4 x = pre.s[j], y = pre.d[j];
                 st4(sS0 + row * LDSB + c4, x);
                 st4(sDS + row * LDSB + c4, y);
                 rowp[j] += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
             }
         }
+        const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
+        pre = fetch(vb + 1);
         __syncthreads();
         if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
             f32x4 r;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w4 + 4 * g + e;
-                r[e] = i < nvalid ? to_f32(vp[rowi(i) * DV + col0 + n]) : 0.f;
-            }
+            for (int e = 0; e < 4; ++e) r[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
             if constexpr (BF) {
                 const float* xa = sK + (16 * w4 + n) * LDK;
                 const float* ea = sEG + (16 * w4 + n) * LDK;
@@ -633,10 +663,10 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * w4 + 4 * g + e;
                 const size_t ri = rowi(i) * DV + col0 + n;
-                const float dy = dop ? to_f32(dop[ri]) : 0.f;
-                const float sg = sigmoidf_(to_f32(gp[ri]));
+                const float dy = cA[e];
+                const float sg = sigmoidf_(cB[e]);
                 sDO[i * LDB + n] = i < nvalid ? dy * sg : 0.f;
-                if (i < nvalid) dgp[ri] = from_f32<E>(dy * to_f32(op[ri]) * (1.f - sg));
+                if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
             }
         }
         __syncthreads();
