@@ -157,3 +157,28 @@ def test_bf16_backward_full_medium_workload_sampled_heads():
         note(f"  (b={b}, h={h}) " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
         for n, e in errs.items():
             assert e <= TOL["bf16"], (b, h, n, e)
+
+
+def test_backward_floored_channels_and_long_sequence():
+    """fp32, 1,000 tokens (16 chunks, a ragged tail): the gradients stay within
+    the fp32 bound over many chunk hand-offs, and dlog_alpha is exactly zero
+    wherever the retention floor binds (log_alpha <= floor)."""
+    B, T, H, d = 1, 1000, 2, 64
+    inp = make_inputs(B, T, H, d, d, io_dtype="f32", seed=901, alpha_min=0.95, logit_mu=-3.0, with_state0=True)
+    floored = inp.log_alpha <= inp.log_alpha_min
+    assert floored.any() and (~floored).any()
+    f = lambda a: to_f64(a, "f32")
+    rng = np.random.default_rng(902)
+    do = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    ds = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    ref = oracle.kda_grad(f(inp.q), f(inp.k), f(inp.v), inp.log_alpha, inp.beta, f(inp.g), inp.log_alpha_min,
+                          inp.state0, d_out=do.astype(np.float64), d_state=ds)
+    dev = kda.to_device(inp)
+    note(f"[backward] B={B} T={T} H={H} d={d} f32, {floored.mean():.0%} of decays floored")
+    gr = kda.backward(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["g"], inp.log_alpha_min,
+                      state_in=dev["state0"], d_out=_dev(do, "f32"), d_state=_dev(ds, "f32"))
+    torch.cuda.synchronize()
+    _check(gr, ref, "f32")
+    dla = gr["dlog_alpha"].cpu().numpy()
+    assert np.all(dla[floored] == 0.0)
+    assert np.count_nonzero(dla[~floored]) > 0.9 * (~floored).sum()

@@ -96,3 +96,19 @@ def test_varlen_many_sequences():
         torch.cuda.synchronize()
         assert torch.equal(out[:, a:b], o1), s
         assert torch.equal(st[s:s + 1], st1), s
+
+
+def test_varlen_state_in_place():
+    """state_out may be the same buffer as state_in (resume in place)."""
+    lengths = [70, 0, 129, 5]
+    H, d = 2, 64
+    inp, dev, cu, s0 = _packed(lengths, H, d, "bf16", seed=55)
+    cu_t = torch.from_numpy(cu).cuda()
+    out_ref, st_ref = kda.varlen_prefill(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["g"],
+                                         inp.log_alpha_min, cu_t, state_in=s0)
+    st = s0.clone()
+    ws = kda.varlen_prepare(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], inp.log_alpha_min, cu_t)
+    out, _ = kda.varlen_scan(ws, dev["g"], inp.log_alpha_min, cu_t, state_in=st, state_out=st)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    assert torch.equal(st, st_ref)
