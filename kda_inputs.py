@@ -5,8 +5,8 @@ holds only random draws, the input distributions and dtype rounding; none of
 the mixer's own arithmetic lives here (no retention floor, no cumulative
 decay, no delta-rule step, no output gate).
 
-Distributions (the pages give no numeric workload; these follow the stated
-workload recipes):
+Distributions (the pages give no numeric workload; these are the workload
+recipes this repository uses):
 
 * q, k ~ N(0, 1), then L2-normalised per (token, head) in fp64, then rounded
   to the I/O dtype.  The kernels normalise again; on these inputs that only

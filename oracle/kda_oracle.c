@@ -7,7 +7,7 @@
  * calls it.
  *
  * What it computes (sources are the pages on Kimi K3; none prints a formula,
- * so each step is the plainest reading of the words, listed in the design doc):
+ * so each step below is the plainest reading of the words):
  *
  *   Per (batch b, head h) the memory is a fixed-size matrix S (d_k x d_v)
  *   [lotamate.com "Kimi K3 是如何训练出来的", §一.1: history is compressed

@@ -5,7 +5,7 @@ The pages describe the two-stage chunk method only in words
 cards" (forget gate, q/k normalisation, decay, intra-chunk correction matrix)
 are prepared in parallel; only the state hand-off and the read-out run in
 order].  The algebra below is this repository's derivation of that method
-from the recurrence ("Chunk form"); this fp64 numpy version checks
+from the recurrence; this fp64 numpy version checks
 it against the oracle before any kernel relies on it.  It is test code, not
 part of the library, and shares nothing with the kernels.
 
