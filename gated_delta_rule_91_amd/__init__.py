@@ -7,7 +7,7 @@ stream, and allocates the update-card workspace with PyTorch.  There is no
 CPU or PyTorch fallback: if the library is missing, every call raises.
 
 Entry points (same names as the C ABI, minus the ``kda_`` prefix):
-    workspace_size, chunk_prepare, chunk_scan, segment_summarize,
+    workspace_size, chunk_prepare, chunk_scan, chunk_scan_checkpoints, segment_summarize,
     segment_combine, decode_step, backward_workspace_size, backward,
     varlen_workspace_size, varlen_prepare, varlen_scan
 Conveniences built from them: prefill, segmented_prefill, varlen_prefill.
@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "workspace too small",
           4: "HIP runtime error"}
-EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_segment_summarize",
+EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_chunk_scan_checkpoints",
+           "kda_segment_summarize",
            "kda_segment_combine", "kda_decode_step", "kda_backward_workspace_size", "kda_backward",
            "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan", "kda_status_string")
 
@@ -58,6 +59,7 @@ def lib() -> ctypes.CDLL:
         L.kda_workspace_size.restype = SZ
         L.kda_chunk_prepare.argtypes = [PP, P, P, P, P, P, P, SZ, P]
         L.kda_chunk_scan.argtypes = [PP, P, SZ, P, P, P, P, P]
+        L.kda_chunk_scan_checkpoints.argtypes = [PP, P, SZ, P, P, P, P, I32, P, P]
         L.kda_segment_summarize.argtypes = [PP, P, SZ, P, P, P]
         L.kda_segment_combine.argtypes = [I64, I32, I32, I32, I32, P, P, P, P, P, P]
         L.kda_decode_step.argtypes = [I64, I32, I32, I32, I32, F32, P, P, P, P, P, P, P, P, P]
@@ -156,6 +158,27 @@ def chunk_scan(workspace, g, log_alpha_min: float, state_in=None, out=None, stat
         ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(g), _ptr(state_in), _ptr(out),
         _ptr(state_out), _stream(stream)))
     return out, state_out
+
+
+def chunk_scan_checkpoints(workspace, g, log_alpha_min: float, every: int, state_in=None, out=None,
+                           state_out=None, stream=None):
+    """Stage 2 plus prefix-cache checkpoints.  Returns (out, state_out, checkpoints
+    [B, H, J+1, dk, dv]) with J = ceil(ceil(T/64) / every): entry j < J is the state
+    after 64*every*j tokens, entry J the final state."""
+    torch = _torch()
+    B, T, H, dv = g.shape
+    p = problem(B, T, H, dv, dv, _io_code(g.dtype), log_alpha_min)
+    nc = (T + 63) // 64
+    J = (nc + every - 1) // every
+    if out is None:
+        out = torch.empty_like(g)
+    if state_out is None:
+        state_out = torch.empty((B, H, dv, dv), dtype=torch.float32, device=g.device)
+    ck = torch.empty((B, H, J + 1, dv, dv), dtype=torch.float32, device=g.device)
+    _check("kda_chunk_scan_checkpoints", lib().kda_chunk_scan_checkpoints(
+        ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(g), _ptr(state_in), _ptr(out), _ptr(state_out),
+        int(every), _ptr(ck), _stream(stream)))
+    return out, state_out, ck
 
 
 def segment_summarize(workspace, batch: int, seqlen: int, heads: int, dk: int, io_dtype, log_alpha_min: float,

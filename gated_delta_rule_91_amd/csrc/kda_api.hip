@@ -124,6 +124,27 @@ kda_status kda_chunk_scan(const kda_problem* p, const void* workspace, size_t wo
     return hip_status(launch_scan(p->io_dtype == KDA_BF16, p->dk, false, a, (hipStream_t)stream));
 }
 
+kda_status kda_chunk_scan_checkpoints(const kda_problem* p, const void* workspace, size_t workspace_bytes,
+                                      const void* g, const float* state_in, void* out, float* state_out,
+                                      int32_t every, float* checkpoints, void* stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    if (every < 1) return KDA_ERR_INVALID_ARGUMENT;
+    const bool tokens = p->batch > 0 && p->seqlen > 0;
+    if (!ok_ptr(workspace, tokens) || !ok_ptr(g, tokens) || !ok_ptr(out, tokens) || !ok_opt_ptr(state_in) ||
+        !ok_opt_ptr(state_out) || !ok_ptr(checkpoints, p->batch > 0))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (p->batch == 0) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    ScanArgs a = {};
+    a.ws = static_cast<const char*>(workspace);
+    a.g = g; a.state_in = state_in; a.out = out; a.state_out = state_out;
+    a.states = checkpoints; a.ckpt_every = every;
+    a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p);
+    return hip_status(launch_scan(p->io_dtype == KDA_BF16, p->dk, false, a, (hipStream_t)stream));
+}
+
 kda_status kda_segment_summarize(const kda_problem* p, const void* workspace, size_t workspace_bytes,
                                  float* transition, float* zero_state, void* stream) {
     kda_status st = check_problem(p);

@@ -25,7 +25,8 @@
 // Kernels, in order (the first two are the forward path's own):
 //   1. kda_prepare_kernel     forward update cards
 //   2. kda_scan_kernel        forward hand-off, also storing the state that
-//                             enters every chunk (and out, for dg)
+//                             enters every chunk and the final one (and out,
+//                             for dg)
 //   3. kda_bwd_card_kernel    per chunk, in parallel: the operands of the
 //                             reverse hand-off -- Ke, Qt^T, -Wk^T, dO in MFMA
 //                             operand order and P^T dO in accumulator order
@@ -93,7 +94,7 @@ struct BwdLayout {
         bcards = cards + up(chunks * card);
         out = bcards + up(chunks * bcard);
         states = out + up((size_t)B * T * H * dk * esz);
-        dstates = states + up(chunks * (size_t)dk * dk * 4);
+        dstates = states + up((chunks + (size_t)B * H) * (size_t)dk * dk * 4);   // NC + 1 slots per (b, h)
         total = dstates + up(chunks * (size_t)dk * dk * 4);
     }
     __host__ __device__ static size_t up(size_t x) { return (x + 255) / 256 * 256; }
@@ -415,7 +416,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     // token row of chunk token i (padded tokens re-read the last valid row)
     auto rowi = [&](int i) { return row0 + (size_t)(i < nvalid ? i : nvalid - 1) * H; };
     const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK);
-    const float* S0 = reinterpret_cast<const float*>(a.ws + L.states) + ((size_t)bh * NC + c) * DK * DV;
+    const float* S0 = reinterpret_cast<const float*>(a.ws + L.states) + ((size_t)bh * (NC + 1) + c) * DK * DV;
     const float* dSo = reinterpret_cast<const float*>(a.ws + L.dstates) + ((size_t)bh * NC + c) * DK * DV;
     const E* qp = reinterpret_cast<const E*>(a.q);
     const E* kp = reinterpret_cast<const E*>(a.k);
@@ -1011,6 +1012,7 @@ hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t
         f.ws = a.ws + L.cards;
         f.g = a.g; f.state_in = a.state_in; f.out = a.ws + L.out;
         f.states = reinterpret_cast<float*>(a.ws + L.states);
+        f.ckpt_every = 1;
         f.B = a.B; f.T = a.T; f.H = a.H; f.NC = a.NC;
         e = launch_scan(bf16, dk, false, f, s);
         if (e != hipSuccess) return e;

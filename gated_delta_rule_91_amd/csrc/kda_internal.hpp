@@ -31,7 +31,9 @@ struct ScanArgs {
     float* state_out;        // [B,H,dk,dv] or null
     float* transition;       // summary mode: [B,H,dk,dk]
     float* zero_state;       // summary mode: [B,H,dk,dv]
-    float* states;           // or null; else the state entering every chunk, [B,H,NC,dk,dv]
+    float* states;           // or null; else checkpoints [B,H,ceil(NC/ckpt_every)+1,dk,dv]: slot j is the
+                             // state entering chunk j*ckpt_every, the last slot the final state
+    int ckpt_every;          // chunks between checkpoints (>= 1 when states is set)
     int64_t B, T;            // packed variable-length batches: B = sequences, T = packed tokens
     int H, NC;
     const int32_t* cu_seqlens;   // or null (uniform batch); else [B+1] token offsets

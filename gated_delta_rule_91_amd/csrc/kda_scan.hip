@@ -240,8 +240,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     auto step = [&](auto full, const O& cur, int c) {
         constexpr bool FULL = decltype(full)::value;
         asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
-        if constexpr (CKPT) {   // the state entering chunk c, for the backward pass
-            float* dst = a.states + ((size_t)bh * NC + c) * DK * DK + col0 + n;
+        if constexpr (CKPT) {
+            // the state entering chunk c goes to slot ceil(c / every): exact
+            // for checkpoint chunks; any other chunk writes the next slot,
+            // which that slot's own (later) store overwrites -- so the stores
+            // stay unconditional
+            const int every = a.ckpt_every;
+            const int nslot = (NC + every - 1) / every + 1;
+            float* dst = a.states + ((size_t)bh * nslot + (c + every - 1) / every) * DK * DK + col0 + n;
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -382,6 +388,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
                     a.state_out[idx] = S[j][mt][e];
                 }
             }
+    if constexpr (CKPT) {   // the final state in the last checkpoint slot
+        const int every = a.ckpt_every;
+        const int nslot = (NC + every - 1) / every + 1;
+        float* dst = a.states + ((size_t)bh * nslot + nslot - 1) * DK * DK + col0 + n;
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int mt = 0; mt < MTS; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[(size_t)((DK / 4) * w + 16 * mt + 4 * g + e) * DK + 16 * j] = S[j][mt][e];
+    }
 }
 
 // Slices per workgroup: two or four slices share each card fragment (more

@@ -99,6 +99,18 @@ kda_status kda_chunk_scan(const kda_problem* p, const void* workspace, size_t wo
                           const void* g, const float* state_in, void* out, float* state_out,
                           void* stream);
 
+/* kda_chunk_scan that also emits state checkpoints for a prefix cache: the
+ * KDA state is saved at reusable boundaries so a later request that shares
+ * the prefix resumes from it [devpress.csdn.net K3 article §十四: KDA state
+ * checkpoints kept alongside the paged cache].  With NC = ceil(seqlen/64)
+ * chunks and J = ceil(NC / every):
+ *   checkpoints: [B, H, J + 1, dk, dv] fp32; entry j (j < J) is the state
+ *   after the first 64*every*j tokens (entry 0 = state_in, or 0), entry J the
+ *   final state.  every >= 1.  Other arguments as for kda_chunk_scan. */
+kda_status kda_chunk_scan_checkpoints(const kda_problem* p, const void* workspace, size_t workspace_bytes,
+                                      const void* g, const float* state_in, void* out, float* state_out,
+                                      int32_t every, float* checkpoints, void* stream);
+
 /* Per-segment summary of the context-parallel scheme [zuoshipin.com/article/
  * 18261 §三, "KDA 上下文并行" paragraph: each segment reports how it changes an
  * existing memory and what it builds from an empty one].  For every

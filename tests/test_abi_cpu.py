@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -90,6 +90,11 @@ def test_prepare_argument_errors(L):
 def test_scan_summarize_combine_decode_argument_errors(L):
     p = _p()
     ws = L.kda_workspace_size(ctypes.byref(p))
+    ck = lambda every=2, c=FAKE: L.kda_chunk_scan_checkpoints(ctypes.byref(p), FAKE, ws, FAKE, None, FAKE, None,
+                                                              every, c, None)
+    assert ck(every=0) == 1
+    assert ck(c=None) == 1
+    assert ck(c=MISALIGNED) == 1
     assert L.kda_chunk_scan(ctypes.byref(p), FAKE, ws, None, None, FAKE, None, None) == 1
     assert L.kda_chunk_scan(ctypes.byref(p), FAKE, ws, FAKE, MISALIGNED, FAKE, None, None) == 1
     assert L.kda_chunk_scan(ctypes.byref(p), FAKE, ws - 256, FAKE, None, FAKE, None, None) == 3
@@ -124,9 +129,10 @@ def test_backward_workspace_and_argument_errors(L):
     p = _p()
     ws = L.kda_backward_workspace_size(ctypes.byref(p))
     # forward cards, reverse-pass cards (4 x 64x128 + 64x128 bf16 + 128 fp32),
-    # the forward output, and two fp32 states per chunk-head
+    # the forward output, and fp32 states: the one entering every chunk plus
+    # the final one, and the gradient of the state leaving every chunk
     chunks = 2 * 3 * 4
-    assert ws == chunks * 74240 + chunks * 82432 + 2 * 200 * 3 * 128 * 2 + 2 * chunks * 128 * 128 * 4
+    assert ws == chunks * 74240 + chunks * 82432 + 2 * 200 * 3 * 128 * 2 + (2 * chunks + 2 * 3) * 128 * 128 * 4
     assert L.kda_backward_workspace_size(ctypes.byref(_p(seqlen=0))) == 0
     assert L.kda_backward_workspace_size(ctypes.byref(_p(dk=96, dv=96))) == 0
     assert _bwd(L, None, ws) == 1

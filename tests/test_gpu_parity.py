@@ -293,3 +293,35 @@ def test_bitwise_deterministic():
     o1, s1 = gpu_prefill(d, inp.log_alpha_min)
     o2, s2 = gpu_prefill(d, inp.log_alpha_min)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("T,every", [(300, 2), (256, 4), (130, 1), (64, 3)])
+def test_scan_checkpoints_match_prefix_runs(T, every):
+    """Prefix-cache checkpoints: entry j is bit-identical to the final state of
+    a prefill over the first 64*every*j tokens, the last entry to the final
+    state, and resuming from a checkpoint reproduces the rest of the outputs
+    exactly."""
+    note(f"[checkpoints] T={T} every={every}")
+    inp = make_inputs(2, T, 3, 64, 64, io_dtype="bf16", seed=300 + T, alpha_min=0.9, logit_mu=-1.0,
+                      with_state0=True)
+    d = kda.to_device(inp)
+    ws = kda.chunk_prepare(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], inp.log_alpha_min)
+    out, st, ck = kda.chunk_scan_checkpoints(ws, d["g"], inp.log_alpha_min, every, state_in=d["state0"])
+    torch.cuda.synchronize()
+    J = ck.shape[2] - 1
+    assert J == ((T + 63) // 64 + every - 1) // every
+    assert torch.equal(ck[:, :, J], st)
+    assert torch.equal(ck[:, :, 0], d["state0"])
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    for j in range(1, J):
+        t = 64 * every * j
+        _, st_j = kda.prefill(sl(d["q"], 0, t), sl(d["k"], 0, t), sl(d["v"], 0, t), sl(d["log_alpha"], 0, t),
+                              sl(d["beta"], 0, t), sl(d["g"], 0, t), inp.log_alpha_min, state_in=d["state0"])
+        torch.cuda.synchronize()
+        assert torch.equal(ck[:, :, j], st_j), j
+        o_rest, st_rest = kda.prefill(sl(d["q"], t, T), sl(d["k"], t, T), sl(d["v"], t, T),
+                                      sl(d["log_alpha"], t, T), sl(d["beta"], t, T), sl(d["g"], t, T),
+                                      inp.log_alpha_min, state_in=ck[:, :, j].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o_rest, out[:, t:]), j
+        assert torch.equal(st_rest, st), j
