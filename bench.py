@@ -22,6 +22,8 @@ Also reported on the same JSON line:
   * the segmented (context-parallel) prefill of 1,048,576 tokens x 8 heads as
     16 segments: per-call times of prepare, segment summaries, in-order
     combine and the per-segment recompute;
+  * the same hand-off emitting prefix-cache checkpoints every 64 chunks
+    (kda_chunk_scan_checkpoints), beside the plain scan;
   * packed variable-length prefill: the long workload's 65,536 tokens x 32
     heads re-cut into sequences of a seeded length mix (kda_varlen_prepare +
     kda_varlen_scan), tokens/s beside the uniform step;
@@ -188,7 +190,22 @@ def main():
                   "attainable_roofline_frac": FLOP_TOK * th / (ms * 1e-3) / 1e12
                   / min(MFMA_BF16_PEAK_TFLOPS, FLOP_TOK / PATH_BYTES * HBM_PEAK_GBS / 1e3)},
         )
-        del d, ws, out, st
+        # the same hand-off emitting prefix-cache checkpoints every 64 chunks (4,096 tokens)
+        every = 64
+        ckpt_ms = 0.0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        kda.chunk_scan_checkpoints(ws, d["g"], floor, every, out=out, state_out=st)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            _, _, ck = kda.chunk_scan_checkpoints(ws, d["g"], floor, every, out=out, state_out=st)
+        e1.record()
+        torch.cuda.synchronize()
+        ckpt_ms = e0.elapsed_time(e1) / 5
+        log(f"[bench] scan with checkpoints every {every} chunks {ckpt_ms:.3f} ms ({ck.shape[2]} per head)")
+        result["checkpoints"] = {"every_chunks": every, "per_head": int(ck.shape[2]), "scan_ms": ckpt_ms,
+                                 "plain_scan_ms": scan_ms}
+        del d, ws, out, st, ck
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode

@@ -147,7 +147,10 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
 constexpr int kRing4 = 4;
 constexpr int kPrefetch = kRing4 + 1;
 
-template <typename E, int DK, int NTW, bool SUMMARY, bool CKPT>
+// CKPT: 0 no checkpoints; 1 the state entering every chunk (unconditional
+// stores); 2 every ckpt_every chunks (a branch around the stores: the cheaper
+// choice when checkpoints are sparse)
+template <typename E, int DK, int NTW, bool SUMMARY, int CKPT>
 __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     using M = MM<E>;
     using CL = Card<E, DK>;
@@ -240,21 +243,19 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     auto step = [&](auto full, const O& cur, int c) {
         constexpr bool FULL = decltype(full)::value;
         asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
-        if constexpr (CKPT) {
-            // the state entering chunk c goes to slot ceil(c / every): exact
-            // for checkpoint chunks; any other chunk writes the next slot,
-            // which that slot's own (later) store overwrites -- so the stores
-            // stay unconditional
-            const int every = a.ckpt_every;
+        if constexpr (CKPT != 0) {   // the state entering chunk c, to slot c / every
+            const int every = CKPT == 1 ? 1 : a.ckpt_every;
             const int nslot = (NC + every - 1) / every + 1;
-            float* dst = a.states + ((size_t)bh * nslot + (c + every - 1) / every) * DK * DK + col0 + n;
+            if (CKPT == 1 || c % every == 0) {
+                float* dst = a.states + ((size_t)bh * nslot + c / every) * DK * DK + col0 + n;
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
+                for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                for (int mt = 0; mt < MTS; ++mt)
+                    for (int mt = 0; mt < MTS; ++mt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        dst[(size_t)((DK / 4) * w + 16 * mt + 4 * g + e) * DK + 16 * j] = S[j][mt][e];
+                        for (int e = 0; e < 4; ++e)
+                            dst[(size_t)((DK / 4) * w + 16 * mt + 4 * g + e) * DK + 16 * j] = S[j][mt][e];
+            }
         }
         // S operand (B fragments) from the shared copy
         typename M::frag sb[NTW][O::NKD];
@@ -388,8 +389,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
                     a.state_out[idx] = S[j][mt][e];
                 }
             }
-    if constexpr (CKPT) {   // the final state in the last checkpoint slot
-        const int every = a.ckpt_every;
+    if constexpr (CKPT != 0) {   // the final state in the last checkpoint slot
+        const int every = CKPT == 1 ? 1 : a.ckpt_every;
         const int nslot = (NC + every - 1) / every + 1;
         float* dst = a.states + ((size_t)bh * nslot + nslot - 1) * DK * DK + col0 + n;
 #pragma unroll
@@ -412,7 +413,7 @@ inline int pick_ntw(int64_t BH, int NTALL) {
     return (NTALL % 2 == 0 && BH * (NTALL / 2) >= kCUs) ? 2 : 1;
 }
 
-template <typename E, int DK, int NTW, bool SUMMARY, bool CKPT>
+template <typename E, int DK, int NTW, bool SUMMARY, int CKPT>
 hipError_t launch_scan_n(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
@@ -422,7 +423,7 @@ hipError_t launch_scan_n(const ScanArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename E, int DK, bool SUMMARY, bool CKPT = false>
+template <typename E, int DK, bool SUMMARY, int CKPT = 0>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
@@ -437,9 +438,13 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s) {
-    if (a.states) {   // forward pass that also keeps every chunk's entering state
-        if (bf16) return dk == 128 ? launch_scan_t<__bf16, 128, false, true>(a, s) : launch_scan_t<__bf16, 64, false, true>(a, s);
-        return dk == 128 ? launch_scan_t<float, 128, false, true>(a, s) : launch_scan_t<float, 64, false, true>(a, s);
+    if (a.states && a.ckpt_every == 1) {   // the state entering every chunk (the backward pass)
+        if (bf16) return dk == 128 ? launch_scan_t<__bf16, 128, false, 1>(a, s) : launch_scan_t<__bf16, 64, false, 1>(a, s);
+        return dk == 128 ? launch_scan_t<float, 128, false, 1>(a, s) : launch_scan_t<float, 64, false, 1>(a, s);
+    }
+    if (a.states) {   // checkpoints every ckpt_every chunks
+        if (bf16) return dk == 128 ? launch_scan_t<__bf16, 128, false, 2>(a, s) : launch_scan_t<__bf16, 64, false, 2>(a, s);
+        return dk == 128 ? launch_scan_t<float, 128, false, 2>(a, s) : launch_scan_t<float, 64, false, 2>(a, s);
     }
     if (bf16) {
         if (dk == 128) return summary ? launch_scan_t<__bf16, 128, true>(a, s) : launch_scan_t<__bf16, 128, false>(a, s);
