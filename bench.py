@@ -329,12 +329,8 @@ def main():
         import numpy as np
         inp = workload(2)
         dl = kda.to_device(inp, dev)
-        # lengths: log-uniform between 64 and 8,192 tokens (seeded), the last one
-        # taking the remainder, so short and long requests mix as in serving
-        rng = np.random.default_rng(2024)
-        lens = []
-        while sum(lens) < T:
-            lens.append(int(min(T - sum(lens), round(float(np.exp(rng.uniform(np.log(64), np.log(8192))))))))
+        from kda_inputs import varlen_lengths
+        lens = varlen_lengths(T)   # log-uniform 64..8,192 tokens, seeded
         cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
         pv = kda.problem(1, T, H, D, D, kda.KDA_BF16, inp.log_alpha_min)
         wsv = torch.empty(kda.varlen_workspace_size(pv, len(lens)), dtype=torch.uint8, device=dev)

@@ -176,6 +176,17 @@ WORKLOADS = {
 }
 
 
+def varlen_lengths(total: int, seed: int = 2024, lo: int = 64, hi: int = 8192) -> list:
+    """Sequence lengths of a packed batch: log-uniform between lo and hi tokens
+    (seeded), the last one taking the remainder, summing to `total` -- short
+    and long requests mixed as in serving."""
+    rng = np.random.default_rng(seed)
+    lens = []
+    while sum(lens) < total:
+        lens.append(int(min(total - sum(lens), round(float(np.exp(rng.uniform(np.log(lo), np.log(hi))))))))
+    return lens
+
+
 def workload(i: int, **override) -> KdaInputs:
     """Inputs of workload ``i``; keyword overrides (e.g. a shorter ``T``) keep the recipe."""
     w = dict(WORKLOADS[i])

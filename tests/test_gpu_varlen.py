@@ -112,3 +112,31 @@ def test_varlen_state_in_place():
     torch.cuda.synchronize()
     assert torch.equal(out, out_ref)
     assert torch.equal(st, st_ref)
+
+
+def test_varlen_benchmark_configuration_sampled_vs_oracle():
+    """The packed batch the benchmark times: the long workload's 65,536 tokens
+    x 32 heads (d=128, bf16) cut into the seeded log-uniform length mix, in the
+    same launch configuration; the oracle runs on sampled (sequence, head)
+    pairs, each from an empty state."""
+    from kda_inputs import varlen_lengths, workload
+    inp = workload(2)
+    T = inp.q.shape[1]
+    lens = varlen_lengths(T)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    note(f"[varlen] benchmark configuration: {len(lens)} sequences, {T} tokens x 32 heads")
+    dev = kda.to_device(inp)
+    out, st = kda.varlen_prefill(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["g"],
+                                 inp.log_alpha_min, torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    f = lambda x: to_f64(x, "bf16")
+    longest = int(np.argmax(lens))
+    for s, h in [(0, 0), (longest, 17), (len(lens) - 1, 31), (len(lens) // 2, 5)]:
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = (slice(None), slice(a, b), slice(h, h + 1))
+        o_ref, s_ref = oracle.kda_ref(f(inp.q[sl]), f(inp.k[sl]), f(inp.v[sl]), inp.log_alpha[sl], inp.beta[sl],
+                                      f(inp.g[sl]), inp.log_alpha_min)
+        eo = _rel(out[sl].float().cpu().numpy(), o_ref)
+        es = _rel(st[s:s + 1, h:h + 1].cpu().numpy(), s_ref)
+        note(f"  sequence {s} ({b - a} tokens), head {h}: rel-L2 out {eo:.2e} state {es:.2e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (s, h, eo, es)
