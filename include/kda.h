@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, out-of-range floor */
-    KDA_ERR_UNSUPPORTED = 2,        /* shape or dtype this build does not implement */
+    KDA_ERR_UNSUPPORTED = 2,        /* shape or dtype the library does not implement */
     KDA_ERR_WORKSPACE_TOO_SMALL = 3,
     KDA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } kda_status;
