@@ -95,9 +95,7 @@ def main():
                     help="only run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the KDA path is measured on a single GPU; a multi-GPU run "
-              f"would shard heads or sequence segments with no other change (--gpus {args.gpus} requested).",
-              file=sys.stderr)
+        print(f"bench.py measures the KDA path on one GPU only (--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
