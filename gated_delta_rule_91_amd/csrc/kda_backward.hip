@@ -33,8 +33,10 @@
 //   4. kda_bwd_scan_kernel    the reverse hand-off dS <- G dS + Qt^T dO - Wk^T dU
 //                             over the chunks in reverse, one workgroup per
 //                             16-column slice; stores the dS leaving every chunk
-//   5. kda_bwd_grad_kernel    per chunk, in parallel: every token gradient
-//                             from S0, dS and the chunk's inputs (fp32 MFMA)
+//   5. kda_bwd_grad_kernel    per chunk, in parallel (eight waves): every token
+//                             gradient from S0, dS and the chunk's inputs
+//                             (bf16 MFMA for most products with bf16 I/O,
+//                             fp32 MFMA otherwise)
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
