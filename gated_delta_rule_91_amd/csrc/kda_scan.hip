@@ -12,12 +12,12 @@
 //
 // The columns of S never interact, so the chain of one (batch row, head) is
 // split into independent 16-column slices; a workgroup runs one, two or four
-// of them, and its state slices (d_k x 16 fp32 each) live in accumulator
+// of them (eight for summaries, which have no read-out), and its state slices (d_k x 16 fp32 each) live in accumulator
 // registers for the whole sequence.  Four waves share a chain: wave w owns
 // U/O rows 16w..16w+15 and state rows w*d_k/4 .. (w+1)*d_k/4 - 1.  U and the
 // operand copy of S cross waves through LDS (two barriers per chunk); the
 // card operands and the gate values are prefetched from global memory four
-// chunks ahead (three with four slices), straight into registers in MFMA
+// chunks ahead (three with four or more slices), straight into registers in MFMA
 // operand layout (a register ring, so the dependent chunk loop does not wait
 // on memory latency).  Every global load is unconditional: the load counter
 // retires in order, so a load under a branch makes the compiler wait for ALL
@@ -142,7 +142,7 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
 // One workgroup = NTW adjacent 16-column slices of one (batch row, head):
 // the card fragments a wave loads serve all NTW slices.
 // Depth of the operand ring (chunks of card fragments in flight per wave):
-// four, or three for four slices per workgroup (register file), and how far
+// four, or three for four or more slices per workgroup (register file), and how far
 // past the chunk a ring load fetches the L2 prefetch runs.
 constexpr int kRing4 = 4;
 constexpr int kPrefetch = kRing4 + 1;
@@ -428,6 +428,11 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
     if (BH == 0) return hipSuccess;
+    // summaries carry no read-out, so eight slices fit one workgroup: with
+    // bf16 operands at d_k = 128 that halves the workgroups when there are
+    // enough (b, h) pairs to fill the GPU with them
+    if constexpr (SUMMARY && sizeof(E) == 2 && DK == 128)
+        if (BH * (NTALL / 8) >= kCUs) return launch_scan_n<E, DK, 8, SUMMARY, CKPT>(a, s);
     switch (pick_ntw(BH, NTALL)) {
     case 4: return launch_scan_n<E, DK, 4, SUMMARY, CKPT>(a, s);
     case 2: return launch_scan_n<E, DK, 2, SUMMARY, CKPT>(a, s);

@@ -169,10 +169,11 @@ def test_segmented_1m_prefill_sampled_head_vs_oracle():
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
-# H = 4 at d = 128: 32 (row, head) chains of the augmented state, so the
-# summary runs two 16-column slices per workgroup; H = 16: 128 chains, four
-# slices per workgroup (and the recompute too)
-@pytest.mark.parametrize("io,H", [("f32", 3), ("bf16", 3), ("bf16", 4), ("bf16", 16)])
+# With 2 rows x 4 segments the summary sees 8H (segment, head) pairs, each
+# with 16 column tiles of the augmented state.  At d = 128 in bf16: H = 4
+# gives two 16-column slices per workgroup, H = 8 four, H = 16 eight (and
+# four in the recompute)
+@pytest.mark.parametrize("io,H", [("f32", 3), ("bf16", 3), ("bf16", 4), ("bf16", 8), ("bf16", 16)])
 def test_summarize_and_combine_vs_oracle(io, H):
     note(f"[summary/combine] {io} H={H}")
     n_seg, Ts, dk = 4, 96, 64 if io == "f32" else 128
