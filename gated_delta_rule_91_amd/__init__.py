@@ -108,10 +108,45 @@ def _ptr(x) -> Optional[int]:
     return x.data_ptr()
 
 
-def _stream(stream=None) -> int:
+def _stream(stream=None, device=None) -> int:
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return s.cuda_stream
+
+
+def _expect(name: str, x, shape, dtype, device):
+    """Shape, dtype and device of an argument, checked before any pointer is
+    taken: the kernels trust every extent the problem implies."""
+    if x is None:
+        return
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} has dtype {x.dtype}, expected {dtype}")
+    if x.device != device:
+        raise ValueError(f"{name} is on {x.device}, expected {device}")
+
+
+def _expect_workspace(ws, device):
+    torch = _torch()
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise TypeError("the workspace must be a 1-D uint8 tensor")
+    if ws.device != device:
+        raise ValueError(f"the workspace is on {ws.device}, expected {device}")
+
+
+def _expect_prefill_inputs(q, k, v, log_alpha, beta):
+    """q, k, log_alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; q/k/v share a dtype."""
+    torch = _torch()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _io_code(q.dtype)
+    _expect("k", k, (B, T, H, dk), q.dtype, q.device)
+    _expect("v", v, (B, T, H, dv), q.dtype, q.device)
+    _expect("log_alpha", log_alpha, (B, T, H, dk), torch.float32, q.device)
+    _expect("beta", beta, (B, T, H), torch.float32, q.device)
 
 
 def problem(batch: int, seqlen: int, heads: int, dk: int, dv: int, io_dtype: int, log_alpha_min: float,
@@ -134,13 +169,15 @@ def workspace_size(p: KdaProblem) -> int:
 def chunk_prepare(q, k, v, log_alpha, beta, log_alpha_min: float, workspace=None, stream=None):
     """Stage 1: update cards for every chunk.  Returns the workspace (uint8 tensor)."""
     torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
     p = _problem_of(q, v, log_alpha_min)
     nbytes = workspace_size(p)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device)
     _check("kda_chunk_prepare", lib().kda_chunk_prepare(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
+        workspace.numel(), _stream(stream, q.device)))
     return workspace
 
 
@@ -150,13 +187,17 @@ def chunk_scan(workspace, g, log_alpha_min: float, state_in=None, out=None, stat
     torch = _torch()
     B, T, H, dv = g.shape
     p = problem(B, T, H, dv, dv, _io_code(g.dtype), log_alpha_min)
+    _expect_workspace(workspace, g.device)
+    _expect("state_in", state_in, (B, H, dv, dv), torch.float32, g.device)
+    _expect("out", out, g.shape, g.dtype, g.device)
+    _expect("state_out", state_out, (B, H, dv, dv), torch.float32, g.device)
     if out is None:
         out = torch.empty_like(g)
     if state_out is None and want_state:
         state_out = torch.empty((B, H, dv, dv), dtype=torch.float32, device=g.device)
     _check("kda_chunk_scan", lib().kda_chunk_scan(
         ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(g), _ptr(state_in), _ptr(out),
-        _ptr(state_out), _stream(stream)))
+        _ptr(state_out), _stream(stream, g.device)))
     return out, state_out
 
 
@@ -170,6 +211,10 @@ def chunk_scan_checkpoints(workspace, g, log_alpha_min: float, every: int, state
     p = problem(B, T, H, dv, dv, _io_code(g.dtype), log_alpha_min)
     nc = (T + 63) // 64
     J = (nc + every - 1) // every
+    _expect_workspace(workspace, g.device)
+    _expect("state_in", state_in, (B, H, dv, dv), torch.float32, g.device)
+    _expect("out", out, g.shape, g.dtype, g.device)
+    _expect("state_out", state_out, (B, H, dv, dv), torch.float32, g.device)
     if out is None:
         out = torch.empty_like(g)
     if state_out is None:
@@ -177,7 +222,7 @@ def chunk_scan_checkpoints(workspace, g, log_alpha_min: float, every: int, state
     ck = torch.empty((B, H, J + 1, dv, dv), dtype=torch.float32, device=g.device)
     _check("kda_chunk_scan_checkpoints", lib().kda_chunk_scan_checkpoints(
         ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(g), _ptr(state_in), _ptr(out), _ptr(state_out),
-        int(every), _ptr(ck), _stream(stream)))
+        int(every), _ptr(ck), _stream(stream, g.device)))
     return out, state_out, ck
 
 
@@ -186,10 +231,11 @@ def segment_summarize(workspace, batch: int, seqlen: int, heads: int, dk: int, i
     """(transition [B,H,dk,dk], zero_state [B,H,dk,dv]) of each (row, head) from its cards."""
     torch = _torch()
     p = problem(batch, seqlen, heads, dk, dk, _io_code(io_dtype), log_alpha_min)
+    _expect_workspace(workspace, workspace.device)
     A = torch.empty((batch, heads, dk, dk), dtype=torch.float32, device=workspace.device)
     Bz = torch.empty((batch, heads, dk, dk), dtype=torch.float32, device=workspace.device)
     _check("kda_segment_summarize", lib().kda_segment_summarize(
-        ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(A), _ptr(Bz), _stream(stream)))
+        ctypes.byref(p), _ptr(workspace), workspace.numel(), _ptr(A), _ptr(Bz), _stream(stream, workspace.device)))
     return A, Bz
 
 
@@ -197,13 +243,19 @@ def segment_combine(transition, zero_state, state_init=None, stream=None):
     """In-order merge.  transition [B,n,H,dk,dk], zero_state [B,n,H,dk,dv] ->
     (state entering each segment [B,n,H,dk,dv], final state [B,H,dk,dv])."""
     torch = _torch()
+    if transition.dim() != 5 or zero_state.dim() != 5:
+        raise ValueError("transition and zero_state must be [B, n_seg, H, dk, d]")
     B, n, H, dk, _ = transition.shape
     dv = zero_state.shape[-1]
+    dev = transition.device
+    _expect("transition", transition, (B, n, H, dk, dk), torch.float32, dev)
+    _expect("zero_state", zero_state, (B, n, H, dk, dv), torch.float32, dev)
+    _expect("state_init", state_init, (B, H, dk, dv), torch.float32, dev)
     seg_in = torch.empty_like(zero_state)
     fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=zero_state.device)
     _check("kda_segment_combine", lib().kda_segment_combine(
         B, n, H, dk, dv, _ptr(transition), _ptr(zero_state), _ptr(state_init), _ptr(seg_in), _ptr(fin),
-        _stream(stream)))
+        _stream(stream, dev)))
     return seg_in, fin
 
 
@@ -211,13 +263,24 @@ def decode_step(q, k, v, log_alpha, beta, g, state, log_alpha_min: float, out=No
     """One token per sequence: q,k,log_alpha [N,H,dk]; v,g [N,H,dv]; beta [N,H];
     state [N,H,dk,dv] fp32 updated in place.  Returns out [N,H,dv]."""
     torch = _torch()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [N, H, d]")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    dev, io = q.device, q.dtype
+    _io_code(io)
+    _expect("k", k, (N, H, dk), io, dev)
+    _expect("v", v, (N, H, dv), io, dev)
+    _expect("log_alpha", log_alpha, (N, H, dk), torch.float32, dev)
+    _expect("beta", beta, (N, H), torch.float32, dev)
+    _expect("g", g, (N, H, dv), io, dev)
+    _expect("state", state, (N, H, dk, dv), torch.float32, dev)
+    _expect("out", out, (N, H, dv), io, dev)
     if out is None:
         out = torch.empty_like(g)
     _check("kda_decode_step", lib().kda_decode_step(
         N, H, dk, dv, _io_code(q.dtype), float(log_alpha_min), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-        _ptr(beta), _ptr(g), _ptr(state), _ptr(out), _stream(stream)))
+        _ptr(beta), _ptr(g), _ptr(state), _ptr(out), _stream(stream, dev)))
     return out
 
 
@@ -234,11 +297,18 @@ def backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, d
     input of prefill.  Returns a dict with dq, dk, dv, dg (dtype of q), dlog_alpha,
     dbeta (fp32) and dstate0 ([B,H,dk,dv] fp32, None unless want_dstate)."""
     torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
     p = _problem_of(q, v, log_alpha_min)
     B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_in", state_in, (B, H, dk, dv), torch.float32, q.device)
+    _expect("d_out", d_out, (B, T, H, dv), q.dtype, q.device)
+    _expect("d_state", d_state, (B, H, dk, dv), torch.float32, q.device)
     nbytes = backward_workspace_size(p)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device)
     r = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
              dlog_alpha=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta))
     r["dstate0"] = torch.empty((B, H, dk, v.shape[-1]), dtype=torch.float32, device=q.device) if want_dstate \
@@ -247,7 +317,7 @@ def backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, d
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g), _ptr(state_in),
         _ptr(d_out), _ptr(d_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dlog_alpha"]),
         _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace), workspace.numel(),
-        _stream(stream)))
+        _stream(stream, q.device)))
     return r
 
 
@@ -258,10 +328,12 @@ def varlen_workspace_size(p: KdaProblem, n_seq: int) -> int:
     return n
 
 
-def _cu(cu_seqlens):
+def _cu(cu_seqlens, device):
     torch = _torch()
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise TypeError("cu_seqlens must be a non-empty 1-D int32 tensor")
+    if cu_seqlens.device != device:
+        raise ValueError(f"cu_seqlens is on {cu_seqlens.device}, expected {device}")
     return cu_seqlens.numel() - 1
 
 
@@ -269,14 +341,16 @@ def varlen_prepare(q, k, v, log_alpha, beta, log_alpha_min: float, cu_seqlens, w
     """Stage 1 for a packed batch: q, k, v, log_alpha [1, T, H, d], beta [1, T, H];
     cu_seqlens int32 [n_seq+1] on the device.  Returns the workspace."""
     torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
     p = _problem_of(q, v, log_alpha_min)
-    n_seq = _cu(cu_seqlens)
+    n_seq = _cu(cu_seqlens, q.device)
     nbytes = varlen_workspace_size(p, n_seq)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device)
     _check("kda_varlen_prepare", lib().kda_varlen_prepare(
         ctypes.byref(p), n_seq, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(workspace), workspace.numel(), _stream(stream, q.device)))
     return workspace
 
 
@@ -286,14 +360,18 @@ def varlen_scan(workspace, g, log_alpha_min: float, cu_seqlens, state_in=None, o
     torch = _torch()
     B, T, H, dv = g.shape
     p = problem(B, T, H, dv, dv, _io_code(g.dtype), log_alpha_min)
-    n_seq = _cu(cu_seqlens)
+    n_seq = _cu(cu_seqlens, g.device)
+    _expect_workspace(workspace, g.device)
+    _expect("state_in", state_in, (n_seq, H, dv, dv), torch.float32, g.device)
+    _expect("out", out, g.shape, g.dtype, g.device)
+    _expect("state_out", state_out, (n_seq, H, dv, dv), torch.float32, g.device)
     if out is None:
         out = torch.empty_like(g)
     if state_out is None and want_state:
         state_out = torch.empty((n_seq, H, dv, dv), dtype=torch.float32, device=g.device)
     _check("kda_varlen_scan", lib().kda_varlen_scan(
         ctypes.byref(p), n_seq, _ptr(cu_seqlens), _ptr(workspace), workspace.numel(), _ptr(g), _ptr(state_in),
-        _ptr(out), _ptr(state_out), _stream(stream)))
+        _ptr(out), _ptr(state_out), _stream(stream, g.device)))
     return out, state_out
 
 

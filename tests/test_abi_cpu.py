@@ -197,3 +197,55 @@ def test_beta_needs_only_natural_alignment(L):
     if not _have_gpu():
         assert L.kda_chunk_prepare(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, ws, None) == 4
     assert L.kda_chunk_prepare(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, ws, None) == 1
+
+
+def _prefill_args(B=2, T=70, H=3, d=64, io="bfloat16"):
+    import torch
+    dt = getattr(torch, io)
+    return dict(q=torch.zeros(B, T, H, d, dtype=dt), k=torch.zeros(B, T, H, d, dtype=dt),
+                v=torch.zeros(B, T, H, d, dtype=dt), log_alpha=torch.zeros(B, T, H, d),
+                beta=torch.zeros(B, T, H), g=torch.zeros(B, T, H, d, dtype=dt))
+
+
+@pytest.mark.parametrize("bad,err", [
+    (dict(k=("shape", (2, 70, 3, 32))), ValueError),
+    (dict(v=("shape", (2, 69, 3, 64))), ValueError),
+    (dict(log_alpha=("dtype", "bfloat16")), TypeError),
+    (dict(beta=("shape", (2, 70))), ValueError),
+    (dict(k=("dtype", "float32")), TypeError),
+])
+def test_binding_rejects_mismatched_prefill_inputs(L, bad, err):
+    """Every extent the kernels read is implied by q and v: a tensor that does
+    not match them is refused before any pointer reaches the library."""
+    import torch
+    a = _prefill_args()
+    (name, (kind, val)), = bad.items()
+    a[name] = torch.zeros(val, dtype=a[name].dtype) if kind == "shape" else a[name].to(getattr(torch, val))
+    with pytest.raises(err, match=name):
+        kda.chunk_prepare(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], -0.1)
+    with pytest.raises(err, match=name):
+        kda.backward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["g"], -0.1)
+
+
+def test_binding_rejects_mismatched_scan_decode_combine_args(L):
+    import torch
+    a = _prefill_args()
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="state_in"):
+        kda.chunk_scan(ws, a["g"], -0.1, state_in=torch.zeros(2, 3, 64, 32))
+    with pytest.raises(ValueError, match="out"):
+        kda.chunk_scan(ws, a["g"], -0.1, out=torch.zeros(2, 70, 3, 32, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="workspace"):
+        kda.chunk_scan(torch.zeros(4, dtype=torch.float32), a["g"], -0.1)
+    N, H, d = 5, 3, 64
+    q = torch.zeros(N, H, d, dtype=torch.bfloat16)
+    st = torch.zeros(N, H, d, d)
+    with pytest.raises(ValueError, match="state"):
+        kda.decode_step(q, q, q, torch.zeros(N, H, d), torch.zeros(N, H), q, torch.zeros(N, H, d, 32), -0.1)
+    with pytest.raises(TypeError, match="log_alpha"):
+        kda.decode_step(q, q, q, torch.zeros(N, H, d, dtype=torch.bfloat16), torch.zeros(N, H), q, st, -0.1)
+    with pytest.raises(ValueError, match="zero_state"):
+        kda.segment_combine(torch.zeros(1, 4, H, d, d), torch.zeros(1, 3, H, d, d))
+    with pytest.raises(TypeError, match="cu_seqlens"):
+        kda.varlen_prepare(*(_prefill_args(B=1)[n] for n in ("q", "k", "v", "log_alpha", "beta")), -0.1,
+                           torch.zeros(3, dtype=torch.int64))
