@@ -223,11 +223,18 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     // The workgroups of one (row, head) read the same cards; each also pulls
     // its share of the card kPrefetch chunks past the ring into L2 (one dword
     // per 128-byte line), so the ring loads of all of them hit in L2 instead of
-    // all waiting on the same HBM misses.
-    constexpr int NL = (int)(CL::BYTES / 128);                 // lines per card
+    // all waiting on the same HBM misses.  Summaries, which have no read-out,
+    // pull only what all their slices share, Wk and Ke^T.  (The read-out scan
+    // measured slower with only its shared operands pulled, so it pulls the
+    // whole card, Wv and e^gamma_C included.)
+    constexpr size_t RA = SUMMARY ? CL::QT : CL::BYTES;                       // [0, RA): Wk (or all)
+    constexpr size_t RB0 = SUMMARY ? CL::KET : 0, RB1 = SUMMARY ? CL::P : 0;  // Ke^T
+    constexpr int NLA = (int)(RA / 128);
+    constexpr int NL = NLA + (int)((RB1 - RB0) / 128);         // lines pulled per card
     constexpr int LPW = (NL + NWG - 1) / NWG;                  // lines per workgroup
     const int pline = (int)(slot % NWG) * LPW + (w * 64 + lane < LPW ? w * 64 + lane : LPW - 1);
-    const uint32_t poff = (uint32_t)((pline < NL ? pline : NL - 1) * 128);
+    const int pl = pline < NL ? pline : NL - 1;
+    const uint32_t poff = (uint32_t)(pl < NLA ? (size_t)pl * 128 : RB0 + (size_t)(pl - NLA) * 128);
     auto load = [&](O& o, int c) {
         const int cc = c < NC ? c : NC - 1;
         const int64_t t0 = (int64_t)cc * C;
