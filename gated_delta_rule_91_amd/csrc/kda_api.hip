@@ -53,9 +53,16 @@ kda_status device_ready() {
 
 kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// Packed variable-length batches: chunk offsets first, then the cards.
+// Packed variable-length batches: chunk offsets first, then each chunk's
+// sequence index, then the cards.
 size_t varlen_offsets_bytes(int64_t n_seq) { return ((size_t)(n_seq + 1) * 8 + 255) / 256 * 256; }
 int64_t varlen_max_chunks(const kda_problem* p, int64_t n_seq) { return n_chunks(p) + n_seq; }
+size_t varlen_seqmap_bytes(const kda_problem* p, int64_t n_seq) {
+    return ((size_t)varlen_max_chunks(p, n_seq) * 4 + 255) / 256 * 256;
+}
+size_t varlen_cards_offset(const kda_problem* p, int64_t n_seq) {
+    return varlen_offsets_bytes(n_seq) + varlen_seqmap_bytes(p, n_seq);
+}
 
 kda_status check_varlen(const kda_problem* p, int64_t n_seq) {
     kda_status st = check_problem(p);
@@ -204,7 +211,7 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
 
 size_t kda_varlen_workspace_size(const kda_problem* p, int64_t n_seq) {
     if (check_varlen(p, n_seq) != KDA_OK || n_seq == 0) return 0;
-    return varlen_offsets_bytes(n_seq) +
+    return varlen_cards_offset(p, n_seq) +
            (size_t)varlen_max_chunks(p, n_seq) * (size_t)p->heads * card_bytes(p->io_dtype == KDA_BF16, p->dk);
 }
 
@@ -223,7 +230,8 @@ kda_status kda_varlen_prepare(const kda_problem* p, int64_t n_seq, const int32_t
     PrepareArgs a = {};
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.chunk_off = static_cast<int64_t*>(workspace);
-    a.ws = static_cast<char*>(workspace) + varlen_offsets_bytes(n_seq);
+    a.chunk_seq = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + varlen_offsets_bytes(n_seq));
+    a.ws = static_cast<char*>(workspace) + varlen_cards_offset(p, n_seq);
     a.cu_seqlens = cu_seqlens;
     a.B = n_seq; a.T = p->seqlen; a.H = p->heads; a.NC = 0;
     a.floor_ = p->log_alpha_min;
@@ -244,7 +252,7 @@ kda_status kda_varlen_scan(const kda_problem* p, int64_t n_seq, const int32_t* c
     if ((st = device_ready()) != KDA_OK) return st;
     ScanArgs a = {};
     a.chunk_off = static_cast<const int64_t*>(workspace);
-    a.ws = static_cast<const char*>(workspace) + varlen_offsets_bytes(n_seq);
+    a.ws = static_cast<const char*>(workspace) + varlen_cards_offset(p, n_seq);
     a.cu_seqlens = cu_seqlens;
     a.g = g; a.state_in = state_in; a.out = out; a.state_out = state_out;
     a.B = n_seq; a.T = p->seqlen; a.H = p->heads; a.NC = 0;

@@ -21,6 +21,7 @@ struct PrepareArgs {
     float floor_;
     const int32_t* cu_seqlens;   // or null (uniform batch); else [B+1] token offsets
     int64_t* chunk_off;          // with cu_seqlens: [B+1] first chunk of each sequence (written here)
+    int32_t* chunk_seq;          // with cu_seqlens: the sequence of each chunk (written here)
 };
 
 struct ScanArgs {

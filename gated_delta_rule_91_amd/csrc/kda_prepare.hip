@@ -111,8 +111,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
 
     // block -> (b, chunk, h): heads fastest, so neighbouring workgroups read
     // neighbouring pieces of the same token rows.  Packed variable-length
-    // batches number chunks across all sequences (chunk_off, written by the
-    // plan kernel); workgroups past the last chunk have nothing to do.
+    // batches number chunks across all sequences (chunk_off and chunk_seq,
+    // written by the plan kernel); workgroups past the last chunk have
+    // nothing to do.
     const int H = a.H;
     const int64_t wg = blockIdx.x;
     const int h = (int)(wg % H);
@@ -121,13 +122,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
     int c;
     if (a.cu_seqlens) {
         if (rest >= a.chunk_off[a.B]) return;
-        int64_t lo = 0, hi = a.B - 1;   // the sequence holding global chunk `rest`
-        while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) >> 1;
-            if (a.chunk_off[mid] <= rest) lo = mid; else hi = mid - 1;
-        }
-        b = lo;
-        c = (int)(rest - a.chunk_off[lo]);
+        b = a.chunk_seq[rest];   // the sequence holding global chunk `rest`
+        c = (int)(rest - a.chunk_off[b]);
     } else {
         c = (int)(rest % a.NC);
         b = rest / a.NC;
@@ -420,9 +416,15 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
 
 // Chunk offsets of a packed variable-length batch: chunk_off[s] = sum of
 // ceil(len/C) over the sequences before s (one workgroup, a block-wide scan
-// per 256 sequences).
+// per 256 sequences), and chunk_seq[j] = the sequence that global chunk j
+// belongs to, so a prepare workgroup finds its sequence with one load.  The
+// offsets are clamped to maxc = ceil(T/C) + nseq, the chunks the workspace
+// holds: only offsets that decrease somewhere (overlapping sequences) can
+// reach it, and then the later sequences lose chunks instead of sending
+// accesses past the workspace.
 __global__ __launch_bounds__(kThreads) void kda_varlen_plan_kernel(const int32_t* cu, int64_t nseq, int64_t T,
-                                                                  int64_t* chunk_off) {
+                                                                  int64_t maxc, int64_t* chunk_off,
+                                                                  int32_t* chunk_seq) {
     __shared__ int64_t part[kThreads];
     const int t = threadIdx.x;
     if (t == 0) chunk_off[0] = 0;
@@ -443,7 +445,12 @@ __global__ __launch_bounds__(kThreads) void kda_varlen_plan_kernel(const int32_t
             part[t] += x;
             __syncthreads();
         }
-        if (s < nseq) chunk_off[s + 1] = carry + part[t];
+        if (s < nseq) {
+            const int64_t end = carry + part[t] < maxc ? carry + part[t] : maxc;
+            const int64_t first = carry + part[t] - ncs < maxc ? carry + part[t] - ncs : maxc;
+            chunk_off[s + 1] = end;
+            for (int64_t j = first; j < end; ++j) chunk_seq[j] = (int32_t)s;
+        }
         carry += part[kThreads - 1];
         __syncthreads();
     }
@@ -453,11 +460,14 @@ template <typename E, int DK>
 hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t s) {
     if (a.cu_seqlens) {
         if (a.B == 0) return hipSuccess;
-        hipLaunchKernelGGL(kda_varlen_plan_kernel, dim3(1), dim3(kThreads), 0, s, a.cu_seqlens, a.B, a.T, a.chunk_off);
+        const int64_t maxc = (a.T + kChunk - 1) / kChunk + a.B;   // chunks the workspace holds
+        hipLaunchKernelGGL(kda_varlen_plan_kernel, dim3(1), dim3(kThreads), 0, s, a.cu_seqlens, a.B, a.T, maxc,
+                           a.chunk_off, a.chunk_seq);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // packed batches: an upper bound on the chunk count (sum of ceil(len/C) <= ceil(T/C) + B)
+    // packed batches: an upper bound on the chunk count (sum of ceil(len/C) <= ceil(T/C) + B for
+    // non-decreasing offsets; the plan kernel clamps the offsets to it otherwise)
     const int64_t chunks = a.cu_seqlens ? (a.T + kChunk - 1) / kChunk + a.B : a.B * (int64_t)a.NC;
     const int64_t blocks = chunks * a.H;
     if (blocks == 0) return hipSuccess;

@@ -151,8 +151,8 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
  * so no offset array makes an access leave the arrays).  Chunks never straddle
  * two sequences, and every sequence's tail is padded inside the kernels.
  *
- * Workspace bytes: chunk offsets plus at most ceil(seqlen/C) + n_seq chunks'
- * cards per head.  Returns 0 if p is invalid or unsupported (batch != 1), or
+ * Workspace bytes: chunk offsets, a sequence index per chunk and at most
+ * ceil(seqlen/C) + n_seq chunks' cards per head.  Returns 0 if p is invalid or unsupported (batch != 1), or
  * if n_seq is 0. */
 size_t kda_varlen_workspace_size(const kda_problem* p, int64_t n_seq);
 

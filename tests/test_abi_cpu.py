@@ -152,8 +152,9 @@ def test_backward_workspace_and_argument_errors(L):
 
 def test_varlen_workspace_and_argument_errors(L):
     p = _p(batch=1, seqlen=1000)
-    # chunk offsets (11 int64 -> 256 B), then at most ceil(1000/64) + 10 chunks of cards per head
-    assert L.kda_varlen_workspace_size(ctypes.byref(p), 10) == 256 + (16 + 10) * 3 * 74240
+    # chunk offsets (11 int64 -> 256 B), the sequence of each of at most ceil(1000/64) + 10 = 26
+    # chunks (4 B each -> 256 B), then 26 chunks of cards per head
+    assert L.kda_varlen_workspace_size(ctypes.byref(p), 10) == 256 + 256 + (16 + 10) * 3 * 74240
     assert L.kda_varlen_workspace_size(ctypes.byref(_p()), 10) == 0          # batch must be 1
     assert L.kda_varlen_workspace_size(ctypes.byref(p), -1) == 0
     ws = L.kda_varlen_workspace_size(ctypes.byref(p), 10)

@@ -140,3 +140,25 @@ def test_varlen_benchmark_configuration_sampled_vs_oracle():
         es = _rel(st[s:s + 1, h:h + 1].cpu().numpy(), s_ref)
         note(f"  sequence {s} ({b - a} tokens), head {h}: rel-L2 out {eo:.2e} state {es:.2e}")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"], (s, h, eo, es)
+
+
+def test_varlen_overlapping_offsets_stay_inside_the_workspace():
+    """Offsets that go back (sequences 0, 2 and 4 all cover tokens 0..255)
+    need 12 chunks where the workspace holds ceil(256/64) + 5 = 9: the plan
+    clamps the chunk offsets, so the last copy keeps one chunk and no access
+    leaves the workspace.  The complete copies equal an ordinary prefill."""
+    H, d, T = 2, 128, 256
+    note("[varlen] overlapping offsets, 12 chunks for a 9-chunk workspace")
+    inp = make_inputs(1, T, H, d, d, io_dtype="bf16", seed=47, alpha_min=0.9, logit_mu=-1.0)
+    dev = kda.to_device(inp)
+    cu = torch.tensor([0, 256, 0, 256, 0, 256], dtype=torch.int32, device="cuda")
+    out, st = kda.varlen_prefill(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["g"],
+                                 inp.log_alpha_min, cu)
+    o1, st1 = kda.prefill(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["g"], inp.log_alpha_min)
+    first = lambda x: x[:, :64].contiguous()
+    _, st64 = kda.prefill(*(first(dev[n]) for n in ("q", "k", "v", "log_alpha", "beta", "g")), inp.log_alpha_min)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o1)
+    assert torch.equal(st[0:1], st1) and torch.equal(st[2:3], st1)
+    assert torch.equal(st[4:5], st64)   # the clamped copy: its first chunk only
+    assert not st[1].any() and not st[3].any()   # empty sequences from a zero state
