@@ -148,8 +148,10 @@ kda_status kda_decode_step(int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
  * p has batch == 1 and seqlen == the packed token count; sequence s is tokens
  * [cu_seqlens[s], cu_seqlens[s+1]) (cu_seqlens: device int32 [n_seq+1],
  * non-decreasing, from 0 to seqlen; values outside [0, seqlen] are clamped,
- * so no offset array makes an access leave the arrays).  Chunks never straddle
- * two sequences, and every sequence's tail is padded inside the kernels.
+ * and offsets that go back make later sequences lose chunks once the chunk
+ * count reaches what the workspace holds, so no offset array makes an access
+ * leave the arrays or the workspace).  Chunks never straddle two sequences,
+ * and every sequence's tail is padded inside the kernels.
  *
  * Workspace bytes: chunk offsets, a sequence index per chunk and at most
  * ceil(seqlen/C) + n_seq chunks' cards per head.  Returns 0 if p is invalid or unsupported (batch != 1), or
