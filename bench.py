@@ -23,7 +23,9 @@ Also reported on the same JSON line:
     16 segments: per-call times of prepare, segment summaries, in-order
     combine and the per-segment recompute;
   * the same hand-off emitting prefix-cache checkpoints every 64 chunks
-    (kda_chunk_scan_checkpoints), beside the plain scan;
+    (kda_chunk_scan_checkpoints), beside the plain scan, and the last 4,096
+    tokens prefilled again from the checkpoint cached before them (the
+    prefix-cache use: prepare + scan with state_in);
   * packed variable-length prefill: the long workload's 65,536 tokens x 32
     heads re-cut into sequences of a seeded length mix (kda_varlen_prepare +
     kda_varlen_scan), tokens/s beside the uniform step;
@@ -204,7 +206,37 @@ def main():
         log(f"[bench] scan with checkpoints every {every} chunks {ckpt_ms:.3f} ms ({ck.shape[2]} per head)")
         result["checkpoints"] = {"every_chunks": every, "per_head": int(ck.shape[2]), "scan_ms": ckpt_ms,
                                  "plain_scan_ms": scan_ms}
-        del d, ws, out, st, ck
+        # prefix cache in use: the last 4,096 tokens prefilled again from the
+        # checkpoint cached after the first 61,440 (prepare + scan with state_in)
+        new_t = every * C
+        j = (T - new_t) // new_t
+        sl = {n: d[n][:, T - new_t:] for n in ("q", "k", "v", "log_alpha", "beta", "g")}
+        s_cached = ck[:, :, j].contiguous()
+        ws_r = torch.empty(kda.workspace_size(kda.problem(B, new_t, H, D, D, kda.KDA_BF16, floor)),
+                           dtype=torch.uint8, device=dev)
+        out_r = torch.empty_like(sl["g"])
+        st_r = torch.empty_like(st)
+
+        def resume():
+            kda.chunk_prepare(sl["q"], sl["k"], sl["v"], sl["log_alpha"], sl["beta"], floor, workspace=ws_r)
+            kda.chunk_scan(ws_r, sl["g"], floor, state_in=s_cached, out=out_r, state_out=st_r)
+
+        resume()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out_r, out[:, T - new_t:]) and torch.equal(st_r, st))
+        e0.record()
+        for _ in range(10):
+            resume()
+        e1.record()
+        torch.cuda.synchronize()
+        res_ms = e0.elapsed_time(e1) / 10
+        log(f"[bench] resume: {new_t} new tokens from the cached state after {T - new_t} in {res_ms:.3f} ms "
+            f"(identical to the uninterrupted run: {same})")
+        result["resume"] = {"workload": f"kda-prefill B1 T{new_t} H{H} d{D} bf16 resumed from the checkpoint after "
+                                        f"{T - new_t} tokens",
+                            "ms": res_ms, "tokens_per_s": B * new_t / (res_ms * 1e-3),
+                            "identical_to_uninterrupted": same}
+        del d, ws, out, st, ck, sl, s_cached, ws_r, out_r, st_r
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode
