@@ -8,7 +8,8 @@
 //
 // The columns of S evolve independently, so each (batch row, head, block of
 // 16 columns) is one workgroup; the 16-column slice of S stays in LDS across
-// the segments and each step is a d_k x d_k x 16 product in fp32 FMA.  The
+// the segments and each step is a d_k x d_k x 16 product in fp32 FMA, with
+// each thread's whole row of A_n requested before the products.  The
 // work is tiny (n_seg dependent steps per head); it is kept exact in fp32
 // because every later segment starts from its result.
 #include "kda_common.hpp"
@@ -51,16 +52,21 @@ __global__ __launch_bounds__(kThreads) void kda_combine_kernel(CombineArgs a) {
         for (int e = 0; e < CPT; ++e) dst[e] = cur[e];
         const float* Ar = a.A + (sh * DK + i) * DK;
         const float* Br = a.Bz + (sh * DK + i) * DV + col0 + j0;
+        // the whole row of A_n is requested at once, so a step waits on one
+        // memory latency rather than one per 16 bytes
+        f32x4 av[DK / 4];
+#pragma unroll
+        for (int q = 0; q < DK / 4; ++q) av[q] = *reinterpret_cast<const f32x4*>(Ar + 4 * q);
         float acc[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) acc[e] = Br[e];
-        for (int c = 0; c < DK; c += 4) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(Ar + c);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the products
+#pragma unroll
+        for (int q = 0; q < DK / 4; ++q)
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-                for (int e = 0; e < CPT; ++e) acc[e] = fmaf(av[cc], sS[buf][c + cc][j0 + e], acc[e]);
-        }
+                for (int e = 0; e < CPT; ++e) acc[e] = fmaf(av[q][cc], sS[buf][4 * q + cc][j0 + e], acc[e]);
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
             cur[e] = acc[e];
