@@ -151,6 +151,34 @@ def test_long_prefill_sampled_heads_vs_oracle():
     assert torch.isfinite(out).all() and torch.isfinite(st).all()
 
 
+def test_prefix_cache_resume_at_benchmark_size():
+    """B=1, T=65536, H=32, d=128 bf16 (one 16-column slice per workgroup, as
+    the benchmark launches it): checkpoints every 64 chunks equal the
+    plain scan's outputs and final state, and prefilling the rest from the
+    checkpoints after 32,768 and 61,440 tokens reproduces outputs and final
+    state bit for bit."""
+    note("[checkpoints] B=1 T=65536 H=32 d=128, every 64 chunks")
+    inp = workload(2)
+    d = kda.to_device(inp)
+    floor = inp.log_alpha_min
+    T = d["q"].shape[1]
+    ws = kda.chunk_prepare(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], floor)
+    out, st = kda.chunk_scan(ws, d["g"], floor)
+    out_c, st_c, ck = kda.chunk_scan_checkpoints(ws, d["g"], floor, 64)
+    torch.cuda.synchronize()
+    assert ck.shape[2] == 17
+    assert torch.equal(out_c, out) and torch.equal(st_c, st) and torch.equal(ck[:, :, 16], st)
+    assert not ck[:, :, 0].any()
+    for j in (8, 15):
+        t = 4096 * j
+        rest = {n: d[n][:, t:] for n in ("q", "k", "v", "log_alpha", "beta", "g")}
+        o_r, s_r = kda.prefill(rest["q"], rest["k"], rest["v"], rest["log_alpha"], rest["beta"], rest["g"], floor,
+                               state_in=ck[:, :, j].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o_r, out[:, t:]), j
+        assert torch.equal(s_r, st), j
+
+
 @pytest.mark.timeout(900)
 def test_segmented_1m_prefill_sampled_head_vs_oracle():
     """T = 1,048,576, H=8, d=128 as 16 segments of 65,536: prepare -> summarize ->
