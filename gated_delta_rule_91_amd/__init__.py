@@ -207,9 +207,12 @@ def chunk_scan_checkpoints(workspace, g, log_alpha_min: float, every: int, state
     [B, H, J+1, dk, dv]) with J = ceil(ceil(T/64) / every): entry j < J is the state
     after 64*every*j tokens, entry J the final state."""
     torch = _torch()
+    if not isinstance(every, int) or not 1 <= every <= 2 ** 31 - 1:
+        raise ValueError(f"every must be an int in [1, 2**31 - 1], got {every!r}")
     B, T, H, dv = g.shape
     p = problem(B, T, H, dv, dv, _io_code(g.dtype), log_alpha_min)
     nc = (T + 63) // 64
+    every = min(every, max(nc, 1))   # the library clamps the same way; the slots are unchanged
     J = (nc + every - 1) // every
     _expect_workspace(workspace, g.device)
     _expect("state_in", state_in, (B, H, dv, dv), torch.float32, g.device)

@@ -144,6 +144,10 @@ kda_status kda_chunk_scan_checkpoints(const kda_problem* p, const void* workspac
     if (workspace_bytes < kda_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (p->batch == 0) return KDA_OK;
     if ((st = device_ready()) != KDA_OK) return st;
+    // every >= NC gives the same slots as every == NC (entry 0 and the final
+    // state), so clamping keeps the kernel's slot arithmetic small
+    const int64_t nc = n_chunks(p);
+    if ((int64_t)every > nc) every = (int32_t)(nc > 1 ? nc : 1);
     ScanArgs a = {};
     a.ws = static_cast<const char*>(workspace);
     a.g = g; a.state_in = state_in; a.out = out; a.state_out = state_out;

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
         asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
         if constexpr (CKPT != 0) {   // the state entering chunk c, to slot c / every
             const int every = CKPT == 1 ? 1 : a.ckpt_every;
-            const int nslot = (NC + every - 1) / every + 1;
+            const int64_t nslot = ((int64_t)NC + every - 1) / every + 1;
             if (CKPT == 1 || c % every == 0) {
                 float* dst = a.states + ((size_t)bh * nslot + c / every) * DK * DK + col0 + n;
 #pragma unroll
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
             }
     if constexpr (CKPT != 0) {   // the final state in the last checkpoint slot
         const int every = CKPT == 1 ? 1 : a.ckpt_every;
-        const int nslot = (NC + every - 1) / every + 1;
+        const int64_t nslot = ((int64_t)NC + every - 1) / every + 1;
         float* dst = a.states + ((size_t)bh * nslot + nslot - 1) * DK * DK + col0 + n;
 #pragma unroll
         for (int j = 0; j < NTW; ++j)

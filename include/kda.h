@@ -31,7 +31,9 @@
  *    are reentrant and may run concurrently on different streams.
  *  - All checks are synchronous and happen before any launch.  Invalid
  *    arguments return an error and launch nothing.  A failed launch returns
- *    KDA_ERR_HIP.  No data-dependent checks are made: NaN/Inf propagate.
+ *    KDA_ERR_HIP.  No data-dependent checks are made.  A NaN log_alpha entry
+ *    acts as the floor (the maximum with log_alpha_min returns the floor);
+ *    NaN/Inf in every other input propagate.
  *  - Preconditions that are documented but not checked: log_alpha <= 0 and
  *    beta in [0, 1] (then every per-token map is a contraction).
  *  - Supported shapes: d_k == d_v in {64, 128}; chunk == 64; any seqlen >= 0
@@ -106,7 +108,8 @@ kda_status kda_chunk_scan(const kda_problem* p, const void* workspace, size_t wo
  * chunks and J = ceil(NC / every):
  *   checkpoints: [B, H, J + 1, dk, dv] fp32; entry j (j < J) is the state
  *   after the first 64*every*j tokens (entry 0 = state_in, or 0), entry J the
- *   final state.  every >= 1.  Other arguments as for kda_chunk_scan. */
+ *   final state.  every in [1, INT32_MAX]; a value above NC acts as NC
+ *   (J = 1).  Other arguments as for kda_chunk_scan. */
 kda_status kda_chunk_scan_checkpoints(const kda_problem* p, const void* workspace, size_t workspace_bytes,
                                       const void* g, const float* state_in, void* out, float* state_out,
                                       int32_t every, float* checkpoints, void* stream);

@@ -250,3 +250,29 @@ def test_binding_rejects_mismatched_scan_decode_combine_args(L):
     with pytest.raises(TypeError, match="cu_seqlens"):
         kda.varlen_prepare(*(_prefill_args(B=1)[n] for n in ("q", "k", "v", "log_alpha", "beta")), -0.1,
                            torch.zeros(3, dtype=torch.int64))
+
+
+@pytest.mark.skipif(_have_gpu(), reason="only meaningful where no HIP device exists")
+def test_checkpoint_every_accepts_the_whole_int32_range(L):
+    """every up to INT32_MAX is valid (values above the chunk count act as the
+    chunk count); with no device the call gets past validation to the HIP
+    error, and every < 1 is an invalid argument."""
+    p = _p()
+    ws = L.kda_workspace_size(ctypes.byref(p))
+    ck = lambda every: L.kda_chunk_scan_checkpoints(ctypes.byref(p), FAKE, ws, FAKE, None, FAKE, None, every,
+                                                    FAKE, None)
+    for every in (1, 4, 5, 2 ** 31 - 1024, 2 ** 31 - 1):
+        assert ck(every) == 4, every
+    for every in (0, -1, -(2 ** 31)):
+        assert ck(every) == 1, every
+
+
+def test_binding_checks_checkpoint_every():
+    """The binding refuses an `every` the C int32 argument cannot carry (ctypes
+    would truncate 2**32 + 1 to 1 and size the checkpoint tensor wrongly)."""
+    import torch
+    g = torch.zeros(1, 200, 2, 64, dtype=torch.bfloat16)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    for every in (0, -3, 2 ** 31, 2 ** 32 + 1, 1.5):
+        with pytest.raises(ValueError, match="every"):
+            kda.chunk_scan_checkpoints(ws, g, -0.1, every)

@@ -44,6 +44,24 @@ def slice_err(gpu, ref, kind):
     return worst
 
 
+def token_worst(gpu, ref):
+    """Largest per-token error of [B,T,H,d] outputs, relative to the RMS token
+    norm of its (b, h) slice.  A slice-wide relative L2 over 65,536 tokens
+    would hide one wrong token row (about 0.4% of the slice norm); here one
+    fully wrong row scores about 1.4."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.linalg.norm(gpu - ref, axis=-1)           # [B,T,H]
+    rms = np.sqrt(np.mean(np.sum(ref * ref, axis=-1), axis=1, keepdims=True))   # [B,1,H]
+    return float(np.max(err / np.maximum(rms, 1e-300)))
+
+
+# bound on token_worst for bf16 I/O: the slice error is ~5e-3 and the
+# largest of 65,536 per-token errors a few times that; a wrong row or a
+# localised error of a tenth of a token's norm exceeds it
+TOKEN_TOL_BF16 = 0.1
+
+
 def host(x):
     return x.float().cpu().numpy().astype(np.float64)
 
@@ -146,8 +164,10 @@ def test_long_prefill_sampled_heads_vs_oracle():
     o_ref, s_ref = oracle_run(inp, heads=heads)
     eo = slice_err(host(out[:, :, heads]), o_ref, "out")
     es = slice_err(host(st[:, heads]), s_ref, "state")
-    note(f"  rel-L2 out {eo:.2e} state {es:.2e}")
+    et = token_worst(host(out[:, :, heads]), o_ref)
+    note(f"  rel-L2 out {eo:.2e} state {es:.2e}; worst token {et:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    assert et <= TOKEN_TOL_BF16
     assert torch.isfinite(out).all() and torch.isfinite(st).all()
 
 
@@ -169,6 +189,13 @@ def test_prefix_cache_resume_at_benchmark_size():
     assert ck.shape[2] == 17
     assert torch.equal(out_c, out) and torch.equal(st_c, st) and torch.equal(ck[:, :, 16], st)
     assert not ck[:, :, 0].any()
+    # the checkpoint contents against the oracle's state after the same prefix
+    h = 3
+    for j in (8, 15):
+        _, s_ref = oracle_run(inp, heads=[h], T=4096 * j)
+        e = slice_err(host(ck[:, h:h + 1, j]), s_ref, "state")
+        note(f"  checkpoint {j} (head {h}) vs oracle: {e:.2e}")
+        assert e <= TOL["bf16"], j
     for j in (8, 15):
         t = 4096 * j
         rest = {n: d[n][:, t:] for n in ("q", "k", "v", "log_alpha", "beta", "g")}
@@ -193,8 +220,10 @@ def test_segmented_1m_prefill_sampled_head_vs_oracle():
     o_ref, s_ref = oracle_run(inp, heads=heads)
     eo = slice_err(host(out[:, :, heads]), o_ref, "out")
     es = slice_err(host(st[:, heads]), s_ref, "state")
-    note(f"  rel-L2 out {eo:.2e} state {es:.2e}")
+    et = token_worst(host(out[:, :, heads]), o_ref)
+    note(f"  rel-L2 out {eo:.2e} state {es:.2e}; worst token {et:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    assert et <= TOKEN_TOL_BF16
 
 
 # With 2 rows x 4 segments the summary sees 8H (segment, head) pairs, each
@@ -324,14 +353,16 @@ def test_bitwise_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
-@pytest.mark.parametrize("T,every", [(300, 2), (256, 4), (130, 1), (64, 3)])
-def test_scan_checkpoints_match_prefix_runs(T, every):
-    """Prefix-cache checkpoints: entry j is bit-identical to the final state of
-    a prefill over the first 64*every*j tokens, the last entry to the final
+@pytest.mark.parametrize("T,every,io", [(300, 2, "bf16"), (256, 4, "bf16"), (130, 1, "bf16"), (64, 3, "bf16"),
+                                       (300, 2, "f32"), (200, 1, "f32")])
+def test_scan_checkpoints_match_prefix_runs(T, every, io):
+    """Prefix-cache checkpoints: entry j holds the oracle's state after the
+    first 64*every*j tokens (to the I/O dtype's bound), is bit-identical to
+    the final state of a prefill over that prefix, the last entry is the final
     state, and resuming from a checkpoint reproduces the rest of the outputs
     exactly."""
-    note(f"[checkpoints] T={T} every={every}")
-    inp = make_inputs(2, T, 3, 64, 64, io_dtype="bf16", seed=300 + T, alpha_min=0.9, logit_mu=-1.0,
+    note(f"[checkpoints] T={T} every={every} {io}")
+    inp = make_inputs(2, T, 3, 64, 64, io_dtype=io, seed=300 + T, alpha_min=0.9, logit_mu=-1.0,
                       with_state0=True)
     d = kda.to_device(inp)
     ws = kda.chunk_prepare(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], inp.log_alpha_min)
@@ -342,6 +373,12 @@ def test_scan_checkpoints_match_prefix_runs(T, every):
     assert torch.equal(ck[:, :, J], st)
     assert torch.equal(ck[:, :, 0], d["state0"])
     sl = lambda x, a, b: x[:, a:b].contiguous()
+    for j in range(J + 1):
+        t = min(64 * every * j, T)
+        _, s_ref = oracle_run(inp, T=t)
+        e = slice_err(host(ck[:, :, j]), s_ref, "state")
+        note(f"  checkpoint {j} (after {t} tokens) vs oracle: {e:.2e}")
+        assert e <= TOL[io], j
     for j in range(1, J):
         t = 64 * every * j
         _, st_j = kda.prefill(sl(d["q"], 0, t), sl(d["k"], 0, t), sl(d["v"], 0, t), sl(d["log_alpha"], 0, t),
@@ -354,3 +391,19 @@ def test_scan_checkpoints_match_prefix_runs(T, every):
         torch.cuda.synchronize()
         assert torch.equal(o_rest, out[:, t:]), j
         assert torch.equal(st_rest, st), j
+
+
+@pytest.mark.parametrize("every", [2 ** 31 - 1, 2 ** 31 - 1000, 5])
+def test_checkpoints_every_beyond_chunk_count(every):
+    """`every` at or past the chunk count (up to INT32_MAX) gives two entries:
+    the entering state and the final state."""
+    note(f"[checkpoints] every={every}")
+    inp = make_inputs(1, 300, 2, 64, 64, io_dtype="bf16", seed=77, alpha_min=0.9, logit_mu=-1.0, with_state0=True)
+    d = kda.to_device(inp)
+    ws = kda.chunk_prepare(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], inp.log_alpha_min)
+    out, st, ck = kda.chunk_scan_checkpoints(ws, d["g"], inp.log_alpha_min, every, state_in=d["state0"])
+    out2, st2 = kda.chunk_scan(ws, d["g"], inp.log_alpha_min, state_in=d["state0"])
+    torch.cuda.synchronize()
+    assert ck.shape[2] == 2
+    assert torch.equal(ck[:, :, 0], d["state0"]) and torch.equal(ck[:, :, 1], st)
+    assert torch.equal(out, out2) and torch.equal(st, st2)
