@@ -11,6 +11,7 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix):
     segment_combine, decode_step, backward_workspace_size, backward,
     varlen_workspace_size, varlen_prepare, varlen_scan
 Conveniences built from them: prefill, segmented_prefill, varlen_prefill.
+prefill_noalloc calls kda_prefill_noalloc, which needs no workspace.
 """
 from __future__ import annotations
 
@@ -28,7 +29,10 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "w
 EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_chunk_scan_checkpoints",
            "kda_segment_summarize",
            "kda_segment_combine", "kda_decode_step", "kda_backward_workspace_size", "kda_backward",
-           "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan", "kda_status_string")
+           "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan", "kda_prefill_noalloc",
+           "kda_status_string")
+# bytes of kda_prefill_noalloc's fixed per-GPU scratch area (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KdaError(RuntimeError):
@@ -70,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.kda_varlen_workspace_size.restype = SZ
         L.kda_varlen_prepare.argtypes = [PP, I64, P, P, P, P, P, P, P, SZ, P]
         L.kda_varlen_scan.argtypes = [PP, I64, P, P, SZ, P, P, P, P, P]
+        L.kda_prefill_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P]
         for f in EXPORTS[1:-1]:
             if not f.endswith("workspace_size"):
                 getattr(L, f).restype = I32
@@ -389,6 +394,31 @@ def prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, wo
     """Chunked prefill: prepare + scan.  Returns (out, final state)."""
     ws = chunk_prepare(q, k, v, log_alpha, beta, log_alpha_min, workspace=workspace, stream=stream)
     return chunk_scan(ws, g, log_alpha_min, state_in=state_in, stream=stream)
+
+
+def prefill_noalloc(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, out=None, state_out=None,
+                    want_state: bool = True, stream=None):
+    """Chunked prefill through kda_prefill_noalloc: the library takes no
+    workspace and allocates nothing (the update cards go to its fixed per-GPU
+    scratch area).  out and state_out are allocated here unless given.
+    Returns (out, state_out)."""
+    torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_in", state_in, (B, H, dk, dv), torch.float32, q.device)
+    _expect("out", out, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_out", state_out, (B, H, dk, dv), torch.float32, q.device)
+    p = _problem_of(q, v, log_alpha_min)
+    if out is None:
+        out = torch.empty_like(g)
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check("kda_prefill_noalloc", lib().kda_prefill_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g), _ptr(state_in),
+        _ptr(out), _ptr(state_out), _stream(stream, q.device)))
+    return out, state_out
 
 
 def segmented_prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, n_seg: int, state_in=None,

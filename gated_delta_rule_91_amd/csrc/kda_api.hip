@@ -2,16 +2,46 @@
 //
 // Every entry point validates its arguments synchronously, before any
 // launch, maps them to the kernel argument blocks and launches on the
-// caller's stream.  Nothing here allocates or keeps state.
+// caller's stream.  Nothing here allocates.  The only state is the fixed
+// scratch area of kda_prefill_noalloc (below) and its per-device address.
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "kda.h"
 #include "kda_internal.hpp"
 
 using namespace kda;
 
+// Update cards of kda_prefill_noalloc.  Each GPU the library runs on holds
+// its own copy until the process ends.  Host code never uses this name as a
+// device address (on the host it is only a stand-in for the symbol): the
+// address of the current device's copy comes from hipGetSymbolAddress, once
+// per device, and only that address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device (with that device current) and kept.
+kda_status scratch_address(void** addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return KDA_ERR_HIP;
+        g_scratch_addr[dev] = a;
+    }
+    *addr = g_scratch_addr[dev];
+    return KDA_OK;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -292,6 +322,77 @@ kda_status kda_backward(const kda_problem* p, const void* q, const void* k, cons
     a.ws = static_cast<char*>(workspace);
     a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p); a.floor_ = p->log_alpha_min;
     return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, (hipStream_t)stream));
+}
+
+kda_status kda_prefill_noalloc(const kda_problem* p, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const void* g, const float* state_in,
+                               void* out, float* state_out, void* stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->batch > 0 && p->seqlen > 0;
+    if (!ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) || !ok_ptr(log_alpha, tokens) ||
+        !ok_beta(beta, tokens) || !ok_ptr(g, tokens) || !ok_ptr(out, tokens) || !ok_opt_ptr(state_in) ||
+        !ok_opt_ptr(state_out))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (p->batch == 0 || (!tokens && !state_out)) return KDA_OK;
+    const bool bf16 = p->io_dtype == KDA_BF16;
+    const int64_t NC = n_chunks(p);
+    hipStream_t s = (hipStream_t)stream;
+    if (NC == 0) {   // no tokens: state_out = state_in (or 0); no cards
+        if ((st = device_ready()) != KDA_OK) return st;
+        ScanArgs a = {};
+        a.state_in = state_in; a.state_out = state_out;
+        a.B = p->batch; a.T = 0; a.H = p->heads; a.NC = 0;
+        return hip_status(launch_scan(bf16, p->dk, false, a, s));
+    }
+    const size_t BH = (size_t)p->batch * (size_t)p->heads;
+    const size_t per_chunk = BH * card_bytes(bf16, p->dk);   // cards of one chunk index, all (row, head)
+    // chunks per pass: all of them if their cards fit; otherwise as many as
+    // fit beside the state carried between passes (in state_out when given,
+    // else at the front of the scratch area)
+    const size_t state_bytes = state_out ? 0 : (BH * (size_t)p->dk * (size_t)p->dv * 4 + 255) / 256 * 256;
+    int64_t per_pass = (int64_t)(KDA_NOALLOC_SCRATCH_BYTES / per_chunk);
+    size_t cards_off = 0;
+    if (per_pass < NC) {
+        if (state_bytes >= KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+        per_pass = (int64_t)((KDA_NOALLOC_SCRATCH_BYTES - state_bytes) / per_chunk);
+        cards_off = state_bytes;
+    }
+    if (per_pass < 1) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if ((st = device_ready()) != KDA_OK) return st;
+    void* base = nullptr;
+    if ((st = scratch_address(&base)) != KDA_OK) return st;
+    char* cards = static_cast<char*>(base) + cards_off;
+    float* carry = state_out ? state_out : reinterpret_cast<float*>(base);
+    const size_t esz = bf16 ? 2 : 4;
+    const int64_t T = p->seqlen;
+    const int H = p->heads;
+    for (int64_t c0 = 0; c0 < NC; c0 += per_pass) {
+        const int64_t c1 = c0 + per_pass < NC ? c0 + per_pass : NC;
+        const int64_t t0 = c0 * 64, t1 = c1 * 64 < T ? c1 * 64 : T;
+        const size_t tok = (size_t)t0 * (size_t)H;   // row-0 offset of the range, in token-heads
+        PrepareArgs pa = {};
+        pa.q = static_cast<const char*>(q) + tok * p->dk * esz;
+        pa.k = static_cast<const char*>(k) + tok * p->dk * esz;
+        pa.v = static_cast<const char*>(v) + tok * p->dv * esz;
+        pa.log_alpha = log_alpha + tok * p->dk;
+        pa.beta = beta + tok;
+        pa.ws = cards;
+        pa.B = p->batch; pa.T = t1 - t0; pa.row_stride = T; pa.H = H; pa.NC = (int)(c1 - c0);
+        pa.floor_ = p->log_alpha_min;
+        hipError_t e = launch_prepare(bf16, p->dk, pa, s);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+        ScanArgs sa = {};
+        sa.ws = cards;
+        sa.g = static_cast<const char*>(g) + tok * p->dv * esz;
+        sa.out = static_cast<char*>(out) + tok * p->dv * esz;
+        sa.state_in = c0 == 0 ? state_in : carry;
+        sa.state_out = (c1 == NC && !state_out) ? nullptr : carry;
+        sa.B = p->batch; sa.T = t1 - t0; sa.row_stride = T; sa.H = H; sa.NC = (int)(c1 - c0);
+        e = launch_scan(bf16, p->dk, false, sa, s);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
 }
 
 }  // extern "C"

@@ -128,8 +128,9 @@ struct Card {
 };
 
 // Where one (sequence, head)'s tokens and cards are.
-//  * Uniform batch: row b holds T tokens starting at token b*T; its chunks'
-//    cards start at card (b*H + h)*NC.
+//  * Uniform batch: row b holds T tokens starting at token b*rs (rs = the
+//    arrays' row stride, T unless a call works on a token range of longer
+//    rows); its chunks' cards start at card (b*H + h)*NC.
 //  * Packed variable-length batch: sequence s holds tokens [cu[s], cu[s+1])
 //    of one packed row (offsets clamped into [0, T], so no offset array can
 //    send an access outside the arrays); its NC_s chunks' cards start at
@@ -145,8 +146,8 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int64_t s, int64_t
     st = a < 0 ? 0 : (a > T ? T : a);
     en = b < st ? st : (b > T ? T : b);
 }
-__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, const int64_t* chunk_off, int64_t T, int NC,
-                                            int64_t b, int h, int H) {
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, const int64_t* chunk_off, int64_t T, int64_t rs,
+                                            int NC, int64_t b, int h, int H) {
     SeqSpan r;
     if (cu) {
         int64_t st, en;
@@ -156,7 +157,7 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, const int64_t* ch
         r.nc = (int)(chunk_off[b + 1] - chunk_off[b]);
         r.card0 = chunk_off[b] * H + (int64_t)h * r.nc;
     } else {
-        r.tok0 = b * T;
+        r.tok0 = b * (rs > 0 ? rs : T);
         r.len = T;
         r.nc = NC;
         r.card0 = (b * H + h) * (int64_t)NC;

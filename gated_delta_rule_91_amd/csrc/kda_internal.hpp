@@ -17,6 +17,7 @@ struct PrepareArgs {
     const float* beta;
     char* ws;
     int64_t B, T;            // packed variable-length batches: B = sequences, T = packed tokens
+    int64_t row_stride;      // uniform batch: tokens between batch rows of the arrays (0 = T)
     int H, NC;
     float floor_;
     const int32_t* cu_seqlens;   // or null (uniform batch); else [B+1] token offsets
@@ -36,6 +37,7 @@ struct ScanArgs {
                              // state entering chunk j*ckpt_every, the last slot the final state
     int ckpt_every;          // chunks between checkpoints (>= 1 when states is set)
     int64_t B, T;            // packed variable-length batches: B = sequences, T = packed tokens
+    int64_t row_stride;      // uniform batch: tokens between batch rows of g and out (0 = T)
     int H, NC;
     const int32_t* cu_seqlens;   // or null (uniform batch); else [B+1] token offsets
     const int64_t* chunk_off;    // with cu_seqlens: [B+1] first chunk of each sequence

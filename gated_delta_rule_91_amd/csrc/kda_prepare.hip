@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
         c = (int)(rest % a.NC);
         b = rest / a.NC;
     }
-    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.NC, b, h, H);
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.row_stride, a.NC, b, h, H);
     const int64_t tok0 = (int64_t)c * C;
     char* card = a.ws + (size_t)(sp.card0 + c) * CL::BYTES;
 

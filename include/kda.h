@@ -27,8 +27,9 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous on it; buffers must stay alive until the work completes.
  *  - The caller owns all memory, including the workspace.  Nothing on the
- *    path allocates, and the library keeps no mutable global state, so calls
- *    are reentrant and may run concurrently on different streams.
+ *    path allocates, and apart from kda_prefill_noalloc's fixed scratch area
+ *    the library keeps no mutable global state, so calls are reentrant and
+ *    may run concurrently on different streams.
  *  - All checks are synchronous and happen before any launch.  Invalid
  *    arguments return an error and launch nothing.  A failed launch returns
  *    KDA_ERR_HIP.  No data-dependent checks are made.  A NaN log_alpha entry
@@ -199,6 +200,30 @@ kda_status kda_backward(const kda_problem* p, const void* q, const void* k, cons
                         const void* d_out, const float* d_state, void* dq, void* dk, void* dv,
                         float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the fixed device scratch area of kda_prefill_noalloc (per GPU). */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* Chunked prefill (kda_chunk_prepare + kda_chunk_scan) that allocates
+ * nothing and takes no workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The update cards go to a fixed scratch area of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  Tokens are processed in ranges of whole chunks
+ * whose cards for all (row, head) fit that area; between ranges the state
+ * travels in state_out, or, when state_out is NULL, at the front of the area.
+ * Results are the same as kda_chunk_prepare + kda_chunk_scan on the same
+ * inputs.
+ *   q, k, v, log_alpha, beta, g, out, state_in, state_out: as for
+ *   kda_chunk_prepare and kda_chunk_scan (state_out may equal state_in).
+ * Returns KDA_ERR_WORKSPACE_TOO_SMALL, launching nothing, when the cards of
+ * one chunk for every (row, head) (B*H cards of 74,240 bytes at bf16 d=128)
+ * do not fit the area beside the carried state.  Every call on a GPU uses
+ * that GPU's one area, which keeps the last call's contents: calls that
+ * overlap on one GPU (other streams, other threads) race, so serialise them. */
+kda_status kda_prefill_noalloc(const kda_problem* p, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const void* g,
+                               const float* state_in, void* out, float* state_out, void* stream);
 
 /* Static text for a status code. */
 const char* kda_status_string(kda_status s);

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -276,3 +276,22 @@ def test_binding_checks_checkpoint_every():
     for every in (0, -3, 2 ** 31, 2 ** 32 + 1, 1.5):
         with pytest.raises(ValueError, match="every"):
             kda.chunk_scan_checkpoints(ws, g, -0.1, every)
+
+
+def test_prefill_noalloc_rejects_what_its_scratch_cannot_hold(L):
+    """kda_prefill_noalloc needs the cards of one chunk for every (row, head)
+    to fit its fixed scratch area beside the carried state; larger batches
+    are refused before any launch, and bad pointers as for prefill."""
+    card = 74240
+    assert kda.NOALLOC_SCRATCH_BYTES // card == 903
+    call = lambda pr, so=None, q=FAKE: L.kda_prefill_noalloc(ctypes.byref(pr), q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                            None, FAKE, so, None)
+    assert call(_p(batch=904, heads=1)) == 3
+    assert call(_p(batch=1, heads=904), so=FAKE) == 3
+    assert call(_p(), q=None) == 1
+    assert call(_p(), q=MISALIGNED) == 1
+    assert call(_p(log_alpha_min=0.5)) == 1
+    assert call(_p(dk=64, dv=128)) == 2
+    if not _have_gpu():   # valid arguments get past validation to the (missing) device
+        assert call(_p(batch=903, heads=1), so=FAKE) == 4
+        assert call(_p()) == 4
