@@ -32,7 +32,9 @@ Also reported on the same JSON line:
   * the backward pass (gradients of every prefill input and of the initial
     state) on the medium prefill workload B=4, T=4,096, H=16, d=128 bf16:
     ms per call and token-heads/s, beside the forward on the same inputs;
-  * cpu_baseline: the fp64 oracle timed on the host over the whole long workload.
+  * cpu_baseline: the fp64 oracle (its source compiled -march=native for the
+    host) timed over the whole long workload on the CPU share given to the
+    job, with the host's CPU count and model.
 """
 from __future__ import annotations
 
@@ -67,6 +69,16 @@ def src_hash(*names):
         with open(os.path.join(ROOT, "gated_delta_rule_91_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def traffic_for(kernel: str, src: str, tokens_heads: int):
@@ -177,7 +189,13 @@ def main():
                     "chunk": C, "state": "fp32", "parallelism": "single GPU"},
             roofline={"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_token_head": dbytes,
-                      "avg_launch_ms": dms, "traffic": traffic_for(dom, shash[dom], th)},
+                      "avg_launch_ms": dms, "traffic": traffic_for(dom, shash[dom], th),
+                      # the whole step against the same peaks: the path's algorithmic
+                      # bytes (1,796 per token-head) and FLOPs over ms_per_step
+                      "path_frac": PATH_BYTES * th / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "path_mfma_frac_bf16": FLOP_TOK * th / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      "path_mfma_frac_ceiling": min(1.0, FLOP_TOK / PATH_BYTES * HBM_PEAK_GBS / 1e3
+                                                    / MFMA_BF16_PEAK_TFLOPS)},
             kernels_ms={"kda_prepare_kernel": prep_ms, "kda_scan_kernel": scan_ms},
             path={"algorithmic_bytes_per_token_head": PATH_BYTES,
                   "hbm_GBps": PATH_BYTES * th / (ms * 1e-3) / 1e9,
@@ -439,22 +457,37 @@ def main():
 
     # ------------------------------------------------------------- cpu baseline
     if not args.no_cpu_baseline and not args.decode_only:
+        import tempfile
         import oracle
         from kda_inputs import to_f64
+        # the unmodified oracle source, compiled for this host's CPU; the
+        # thread count is the CPU share this job was given
+        try:
+            oracle.use_library(oracle.build_native(tempfile.mkdtemp(prefix="kda_oracle_")))
+            build = "gcc -O3 -march=native"
+        except Exception as e:   # no compiler on the host: the portable build the checks use
+            build = f"gcc -O3 (portable build; native build failed: {type(e).__name__})"
         sample = workload(2)
         f = lambda a: to_f64(a, "bf16")
         args_o = (f(sample.q), f(sample.k), f(sample.v), sample.log_alpha, sample.beta, f(sample.g),
                   sample.log_alpha_min)
         del sample
-        nthr = oracle.default_threads()
+        nthr = oracle.host_threads()
         t0 = time.perf_counter()
         oracle.kda_ref(*args_o, nthreads=nthr)
         dt = time.perf_counter() - t0
         del args_o
-        result["cpu_baseline"] = {"value": B * T / dt, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
-                                  "sample": f"the whole workload: fp64 step recurrence over all {H} heads x {T} "
-                                            f"tokens ({dt:.1f} s)"}
-        log(f"[bench] oracle {dt:.1f}s on {nthr} threads")
+        try:
+            affinity = len(os.sched_getaffinity(0))
+        except (AttributeError, OSError):
+            affinity = None
+        result["cpu_baseline"] = {
+            "value": B * T / dt, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+            "sample": f"the whole workload: fp64 step recurrence over all {H} heads x {T} tokens ({dt:.1f} s)",
+            "threads_used": nthr, "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "threads_rule": "OMP_NUM_THREADS (the CPU share given to the job) if set, else the affinity mask",
+            "cpu_model": cpu_model(), "build": build}
+        log(f"[bench] oracle {dt:.1f}s on {nthr} threads ({cpu_model()}, {build})")
 
     print(json.dumps(result), flush=True)
 

@@ -21,7 +21,8 @@ import os
 from typing import Optional, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkda.so")
+# another build of the library to load instead (the sanitizer tests set it)
+LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(_PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "workspace too small",

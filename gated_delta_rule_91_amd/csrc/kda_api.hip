@@ -114,8 +114,8 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
         case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KDA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
     }
-    return "unknown status";
 }
 
 size_t kda_workspace_size(const kda_problem* p) {

@@ -58,12 +58,19 @@ typedef enum {
     KDA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, out-of-range floor */
     KDA_ERR_UNSUPPORTED = 2,        /* shape or dtype the library does not implement */
     KDA_ERR_WORKSPACE_TOO_SMALL = 3,
-    KDA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+    KDA_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
+    /* not codes: they give the type the whole int32 range, so any int a
+     * caller passes is a value of it (kda_status_string then reports it unknown) */
+    KDA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    KDA_STATUS_RANGE_MAX_ = 2147483647
 } kda_status;
 
 typedef enum {
     KDA_F32 = 0,                    /* q, k, v, g, out are float32 */
-    KDA_BF16 = 1                    /* q, k, v, g, out are bfloat16 */
+    KDA_BF16 = 1,                   /* q, k, v, g, out are bfloat16 */
+    /* not dtypes: the whole int32 range, so any other value is an invalid argument */
+    KDA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    KDA_DTYPE_RANGE_MAX_ = 2147483647
 } kda_dtype;
 
 typedef struct {

@@ -20,6 +20,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB = os.path.join(_HERE, "libkda_oracle.so")
+# another build of kda_oracle.c to load instead (the sanitizer tests set it)
+_LIB_OVERRIDE = os.environ.get("KDA_ORACLE_LIB")
 _lib = None
 
 
@@ -33,25 +35,47 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_native(dst_dir: str) -> str:
+    """Compile the same source with -march=native into dst_dir (for timing the
+    oracle on the host it runs on; the checks use the portable build)."""
+    out = os.path.join(dst_dir, "libkda_oracle_native.so")
+    subprocess.check_call(["gcc", "-O3", "-march=native", "-std=c11", "-fPIC", "-shared", "-pthread",
+                           _SRC, "-o", out, "-lm"])
+    return out
+
+
+def use_library(path: str) -> None:
+    """Load the oracle from `path` (a build of kda_oracle.c) for later calls."""
+    global _lib
+    _lib = _declare(ctypes.CDLL(path))
+
+
 def _load():
     global _lib
     if _lib is None:
+        if _LIB_OVERRIDE:
+            _lib = _declare(ctypes.CDLL(_LIB_OVERRIDE))
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        I64, I32, F64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
-        lib.kda_oracle_ref.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, P, P, F64, P, P, P, I32]
-        lib.kda_oracle_ref.restype = I32
-        lib.kda_oracle_summary.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, F64, P, P, I32]
-        lib.kda_oracle_summary.restype = I32
-        lib.kda_oracle_combine.argtypes = [I64, I32, I32, I32, I32, P, P, P, P, P]
-        lib.kda_oracle_combine.restype = I32
-        lib.kda_oracle_grad.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, P, P, F64, P, P, P,
-                                        P, P, P, P, P, P, P, I32]
-        lib.kda_oracle_grad.restype = I32
-        _lib = lib
+        _lib = _declare(ctypes.CDLL(_LIB))
     return _lib
+
+
+def _declare(lib):
+    """Argument and result types of the oracle's C functions."""
+    P = ctypes.c_void_p
+    I64, I32, F64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.kda_oracle_ref.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, P, P, F64, P, P, P, I32]
+    lib.kda_oracle_ref.restype = I32
+    lib.kda_oracle_summary.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, F64, P, P, I32]
+    lib.kda_oracle_summary.restype = I32
+    lib.kda_oracle_combine.argtypes = [I64, I32, I32, I32, I32, P, P, P, P, P]
+    lib.kda_oracle_combine.restype = I32
+    lib.kda_oracle_grad.argtypes = [I64, I64, I32, I32, I32, P, P, P, P, P, P, F64, P, P, P,
+                                    P, P, P, P, P, P, P, I32]
+    lib.kda_oracle_grad.restype = I32
+    return lib
 
 
 def _c(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
@@ -64,6 +88,18 @@ def _p(a: Optional[np.ndarray]):
 
 def default_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
+
+
+def host_threads() -> int:
+    """Threads this process may use on the host: the CPU share given to it
+    (OMP_NUM_THREADS when set), else the CPUs in its affinity mask."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
 
 
 def kda_ref(q, k, v, log_alpha, beta, g, log_alpha_min: float, state0=None,
