@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_prepare.hip", "kda_scan.hip", "kda_decode.hip", "kda_combine.hip", "kda_backward.hip"]
+SOURCES = ["kda_api.hip", "kda_prepare.hip", "kda_scan.hip", "kda_scan_wave.hip", "kda_decode.hip", "kda_combine.hip", "kda_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -46,7 +46,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    # --no-undefined: a kernel whose host stub the compiler dropped fails here, not at load time
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

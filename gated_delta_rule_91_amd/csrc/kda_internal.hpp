@@ -95,6 +95,9 @@ size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk);
 hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t s);
 hipError_t launch_prepare(bool bf16, int dk, const PrepareArgs& a, hipStream_t s);
 hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s);
+// segment summaries of bf16 cards at d_k = d_v = 128 with whole 16-column
+// slices of [Bz | A] per wave, spw (1 or 2) slices per wave
+hipError_t launch_summary_wave(int spw, const ScanArgs& a, hipStream_t s);
 hipError_t launch_decode(bool bf16, int dk, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 

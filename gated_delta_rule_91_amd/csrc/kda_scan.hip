@@ -12,8 +12,9 @@
 //
 // The columns of S never interact, so the chain of one (batch row, head) is
 // split into independent 16-column slices; a workgroup runs one, two or four
-// of them (eight for summaries, which have no read-out), and its state slices (d_k x 16 fp32 each) live in accumulator
-// registers for the whole sequence.  Four waves share a chain: wave w owns
+// of them, and its state slices (d_k x 16 fp32 each) live in accumulator
+// registers for the whole sequence.  (Summaries of bf16 d_k = 128 cards with
+// many (row, head) pairs run in kda_scan_wave.hip instead.)  Four waves share a chain: wave w owns
 // U/O rows 16w..16w+15 and state rows w*d_k/4 .. (w+1)*d_k/4 - 1.  U and the
 // operand copy of S cross waves through LDS (two barriers per chunk); the
 // card operands and the gate values are prefetched from global memory four
@@ -444,11 +445,13 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     constexpr int NTALL = SUMMARY ? 2 * (DK / 16) : DK / 16;
     const int64_t BH = a.B * (int64_t)a.H;
     if (BH == 0) return hipSuccess;
-    // summaries carry no read-out, so eight slices fit one workgroup: with
-    // bf16 operands at d_k = 128 that halves the workgroups when there are
-    // enough (b, h) pairs to fill the GPU with them
+    // summaries of bf16 d_k = 128 cards with enough (b, h) pairs to give
+    // every workgroup four or eight slices run one whole slice per wave (or
+    // two): no exchange of the state between waves, operands shared through
+    // an LDS ring.  Measured on 16K-token segments: 0.23 against 0.28 ms at
+    // 32 pairs, 0.49 against 0.72 ms at 128; slower below 32 pairs.
     if constexpr (SUMMARY && sizeof(E) == 2 && DK == 128)
-        if (BH * (NTALL / 8) >= kCUs) return launch_scan_n<E, DK, 8, SUMMARY, CKPT>(a, s);
+        if (BH * 4 >= kCUs / 2) return launch_summary_wave(BH * 2 >= kCUs ? 2 : 1, a, s);
     switch (pick_ntw(BH, NTALL)) {
     case 4: return launch_scan_n<E, DK, 4, SUMMARY, CKPT>(a, s);
     case 2: return launch_scan_n<E, DK, 2, SUMMARY, CKPT>(a, s);

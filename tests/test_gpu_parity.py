@@ -227,9 +227,10 @@ def test_segmented_1m_prefill_sampled_head_vs_oracle():
 
 
 # With 2 rows x 4 segments the summary sees 8H (segment, head) pairs, each
-# with 16 column tiles of the augmented state.  At d = 128 in bf16: H = 4
-# gives two 16-column slices per workgroup, H = 8 four, H = 16 eight (and
-# four in the recompute)
+# with 16 column tiles of the augmented state.  At d = 128 in bf16: H = 3
+# (24 pairs) runs the summaries with two 16-column slices per workgroup
+# (four waves share a slice), H = 4 and H = 8 one whole slice per wave, H =
+# 16 two slices per wave (and four slices per workgroup in the recompute)
 @pytest.mark.parametrize("io,H", [("f32", 3), ("bf16", 3), ("bf16", 4), ("bf16", 8), ("bf16", 16)])
 def test_summarize_and_combine_vs_oracle(io, H):
     note(f"[summary/combine] {io} H={H}")
@@ -261,6 +262,29 @@ def test_summarize_and_combine_vs_oracle(io, H):
                                        inp.state0)
     assert slice_err(host(seg_in).reshape(-1, H, dk, dk), si_ref.reshape(-1, H, dk, dk), "state") < 1e-5
     assert slice_err(host(fin2), f_ref, "state") < 1e-5
+
+
+# Segments shorter than a chunk, one full chunk, a ragged tail and none at
+# all, on both per-wave summary layouts (8 rows x H=4: one slice per wave;
+# 8 rows x H=16: two).  An empty segment is the identity map.
+@pytest.mark.parametrize("H", [4, 16])
+@pytest.mark.parametrize("Ts", [0, 1, 40, 64, 161])
+def test_summary_lengths_vs_oracle(H, Ts):
+    note(f"[summary lengths] rows=8 H={H} T={Ts}")
+    inp = make_inputs(8, Ts, H, 128, 128, io_dtype="bf16", seed=43, alpha_min=0.9, logit_mu=-4.0)
+    d = kda.to_device(inp)
+    ws = kda.chunk_prepare(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], inp.log_alpha_min)
+    A, Bz = kda.segment_summarize(ws, 8, Ts, H, 128, torch.bfloat16, inp.log_alpha_min)
+    torch.cuda.synchronize()
+    if Ts == 0:
+        eye = torch.eye(128, device=DEV).expand(8, H, 128, 128)
+        assert torch.equal(A, eye) and not torch.any(Bz)
+        return
+    f = lambda a: to_f64(a, "bf16")
+    A_ref, B_ref = oracle.kda_summary(f(inp.k), f(inp.v), inp.log_alpha, inp.beta, inp.log_alpha_min)
+    ea, eb = slice_err(host(A), A_ref, "state"), slice_err(host(Bz), B_ref, "state")
+    note(f"  summary A {ea:.2e} Bz {eb:.2e}")
+    assert ea <= TOL["bf16"] and eb <= TOL["bf16"]
 
 
 def _decode_all(d, floor, T):

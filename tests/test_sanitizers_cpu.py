@@ -23,7 +23,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OUT = os.path.join(ROOT, "_build", "sanitize")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["kda_api", "kda_prepare", "kda_scan", "kda_decode", "kda_combine", "kda_backward"]
+SOURCES = ["kda_api", "kda_prepare", "kda_scan", "kda_scan_wave", "kda_decode", "kda_combine", "kda_backward"]
 
 
 def _run(cmd, env=None, timeout=900):
