@@ -137,7 +137,16 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
     if (w >= kComputeW) {
         // ---------------- loader waves ----------------
         const int lw = w - kComputeW;
-        constexpr int NL = (int)(CL::BYTES / 128);
+        // lines of the card the summaries read: Wk, Ke^T, then Wv and e^gamma_C
+        // (Qt and P, between them, are only read by the read-out scan)
+        constexpr int NL_WK = (int)((CL::QT - CL::WK) / 128), NL_KE = (int)((CL::P - CL::KET) / 128);
+        constexpr int NL = NL_WK + NL_KE + (int)((CL::BYTES - CL::WV) / 128);
+        static_assert(CL::WK % 128 == 0 && CL::KET % 128 == 0 && CL::WV % 128 == 0 && CL::BYTES % 128 == 0, "line map");
+        auto line_off = [](int li) -> size_t {
+            return li < NL_WK ? CL::WK + (size_t)li * 128
+                 : li < NL_WK + NL_KE ? CL::KET + (size_t)(li - NL_WK) * 128
+                 : CL::WV + (size_t)(li - NL_WK - NL_KE) * 128;
+        };
         constexpr int LPW = (NL + NWG - 1) / NWG;
         constexpr int PPL = (LPW + 64 * kLoadersW - 1) / (64 * kLoadersW);
         lds_c* const dump_l = (lds_c*)dump + lw * 256;
@@ -163,7 +172,8 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
             // e^gamma_C (DK floats)
             __builtin_amdgcn_global_load_lds(cards + (size_t)cc * CL::BYTES + CL::GC + (gc_mine ? lw * 256 : 0) + lane * 4,
                                              gc_mine ? dst + WR::GC_OFF + lw * 256 : dump_l, 4, 0, 0);
-            // L2 pull of a later card: each workgroup of the chain a disjoint share of its lines
+            // L2 pull of a later card's lines that are read here: each workgroup
+            // of the chain a disjoint share
             const int cp = c + kPullAheadW < NC ? c + kPullAheadW : NC - 1;
             const char* pbase = cards + (size_t)cp * CL::BYTES;
 #pragma unroll
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
                 int line = wgi * LPW + (i * kLoadersW + lw) * 64 + lane;
                 line = line < (wgi + 1) * LPW ? line : (wgi + 1) * LPW - 1;
                 line = line < NL ? line : NL - 1;
-                __builtin_amdgcn_global_load_lds(pbase + (size_t)line * 128, dump_l, 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(pbase + line_off(line), dump_l, 4, 0, 0);
             }
         };
         // loads per chunk and loader wave, and the s_waitcnt encoding (gfx9:
