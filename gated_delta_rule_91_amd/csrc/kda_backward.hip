@@ -328,9 +328,12 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
 // go through in 16-column blocks; the products that contract over the value
 // columns accumulate in registers across the blocks.  Wave w works on token
 // tile w % 4; the two halves of the workgroup (w / 4) run independent
-// products side by side (R | dO and dg;  U | Ke dS + P^T dO;  dU~ | dO U^T;
+// products side by side (R | dO, dg and Ke dS;  U | + P^T dO;  dU~ | dO U^T;
 // dU~ U^T) and split the d_k-wide outputs by channel tile, so two waves share
-// each SIMD and either can issue while the other waits.  With bf16 I/O the
+// each SIMD and either can issue while the other waits.  Triangular products
+// run over all four 16-token blocks (the blocks past the diagonal are zero in
+// LDS), and no global load sits under a branch, so loads stay in flight
+// across the phases.  With bf16 I/O the
 // Gram matrices, R, U, Ke dS + P^T dO, dU~, dM, dP and the three products
 // that contract over the value columns take bf16 operands (16x16x16 MFMA,
 // fp32 accumulation), the operand precision of the forward cards; the
@@ -424,59 +427,74 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     const E* kp = reinterpret_cast<const E*>(a.k);
 
     // ---- 1: norms, k^, q^, e^gamma, beta ----
+    // Every global input of the phase is requested first (one memory round
+    // trip).  Thread t holds the four-channel pieces jj of tokens
+    // (t + jj * NTH) / (DK / 4); the DK / 4 pieces of a token sit in adjacent
+    // lanes, which sum its squared norms with shuffles.
+    constexpr int TPL = DK / 4;               // lanes per token
+    constexpr int NPC = C * TPL / NTH;        // pieces per thread
+    static_assert(NTH % TPL == 0 && (C * TPL) % NTH == 0, "piece layout");
+    f32x4 kx[NPC], qx[NPC], lx[NPC];
 #pragma unroll
-    for (int ii = 0; ii < C / 8; ++ii) {   // wave w: tokens 8w .. 8w+7
-        const int i = (C / 8) * w + ii;
-        const size_t r = rowi(i);
+    for (int jj = 0; jj < NPC; ++jj) {
+        const int idx = t + jj * NTH, i = idx / TPL, ch = (idx % TPL) * 4;
+        const size_t r = rowi(i) * DK + ch;
+        kx[jj] = ld4(kp + r);
+        qx[jj] = ld4(qp + r);
+        lx[jj] = *reinterpret_cast<const f32x4*>(a.log_alpha + r);
+    }
+    const float bv = a.beta[rowi(t % C)];   // every thread loads (clamped): no load under a branch
+    for (int idx = t; idx < C * LDC; idx += NTH) sT[idx] = 0.f;   // T's upper tiles stay zero
+    if (t < C) sBeta[t] = t < nvalid ? bv : 0.f;
+#pragma unroll
+    for (int jj = 0; jj < NPC; ++jj) {
+        const int idx = t + jj * NTH, i = idx / TPL, ch = (idx % TPL) * 4;
         float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int e = 0; e < DK / 64; ++e) {
-            const float kk = to_f32(kp[r * DK + lane * (DK / 64) + e]), qq = to_f32(qp[r * DK + lane * (DK / 64) + e]);
-            sk += kk * kk;
-            sq += qq * qq;
+        for (int e = 0; e < 4; ++e) {
+            sk += kx[jj][e] * kx[jj][e];
+            sq += qx[jj][e] * qx[jj][e];
         }
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
+        for (int off = 1; off < TPL; off <<= 1) {
             sk += __shfl_xor(sk, off);
             sq += __shfl_xor(sq, off);
         }
-        if (lane == 0) {
-            sNk[i] = sqrtf(sk);
-            sNq[i] = sqrtf(sq);
-            sRk[i] = 1.f / fmaxf(sqrtf(sk), 1e-6f);
-            sRq[i] = 1.f / fmaxf(sqrtf(sq), 1e-6f);
+        const float nk = sqrtf(sk), nq = sqrtf(sq);
+        const float rk = 1.f / fmaxf(nk, 1e-6f), rq = 1.f / fmaxf(nq, 1e-6f);
+        if (idx % TPL == 0) {
+            sNk[i] = nk;
+            sNq[i] = nq;
+            sRk[i] = rk;
+            sRq[i] = rq;
         }
+        const bool ok = i < nvalid;   // padded tokens: k^ = q^ = 0, no decay
+        st4(sK + i * LDK + ch, ok ? kx[jj] * rk : f32x4{0.f, 0.f, 0.f, 0.f});
+        st4(sQ + i * LDK + ch, ok ? qx[jj] * rq : f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 lam;   // floored log-decay in base 2
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lam[e] = ok ? fmaxf(lx[jj][e], a.floor_) * kLog2e : 0.f;
+        st4(sEG + i * LDK + ch, lam);
     }
-    if (t < C) sBeta[t] = t < nvalid ? a.beta[rowi(t)] : 0.f;
-    for (int idx = t; idx < C * LDC; idx += NTH) sT[idx] = 0.f;   // T's upper tiles stay zero
     __syncthreads();
-    // q^ (zero on padded tokens), four channels per item
+    // q^ again after the column loop (its LDS rows hold the state blocks meanwhile)
     auto load_qhat = [&]() {
-        for (int idx = t; idx < C * DK / 4; idx += NTH) {
-            const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
+#pragma unroll
+        for (int jj = 0; jj < NPC; ++jj) {
+            const int idx = t + jj * NTH;
+            const int i = idx / TPL, ch = (idx % TPL) * 4;
             const f32x4 x = ld4(qp + rowi(i) * DK + ch);
             st4(sQ + i * LDK + ch, i < nvalid ? x * sRq[i] : f32x4{0.f, 0.f, 0.f, 0.f});
         }
     };
-    load_qhat();
-    for (int idx = t; idx < C * DK / 4; idx += NTH) {
-        const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
-        const size_t r = rowi(i) * DK + ch;
-        const bool ok = i < nvalid;
-        const f32x4 x = ld4(kp + r);
-        const f32x4 la = *reinterpret_cast<const f32x4*>(a.log_alpha + r);
-        st4(sK + i * LDK + ch, ok ? x * sRk[i] : f32x4{0.f, 0.f, 0.f, 0.f});
-        // floored log-decay in base 2 (padded tokens add nothing)
-        f32x4 lam;
+    if (t < DK) {   // e^gamma: cumulative log-decay of channel t (the column read first, then summed)
+        float col[C];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lam[e] = ok ? fmaxf(la[e], a.floor_) * kLog2e : 0.f;
-        st4(sEG + i * LDK + ch, lam);
-    }
-    __syncthreads();
-    if (t < DK) {   // e^gamma: cumulative log-decay of channel t
+        for (int i = 0; i < C; ++i) col[i] = sEG[i * LDK + t];
         float run = 0.f;
+#pragma unroll
         for (int i = 0; i < C; ++i) {
-            run += sEG[i * LDK + t];
+            run += col[i];
             sEG[i * LDK + t] = __builtin_amdgcn_exp2f(run);
         }
     }
@@ -491,40 +509,34 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     // diag(beta) A -> sT; half 1: P = Qt Kh^T -> sP ----
     f32x4 As[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        As[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (j <= w4) {
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF) {   // rows of Kt (or Qt) against rows of Kh, 16 channels per step
-                const float* xa = (half == 0 ? sK : sQ) + (16 * w4 + n) * LDK;
-                const float* ea = sEG + (16 * w4 + n) * LDK;
-                const float* kb = sK + (16 * j + n) * LDK;
-                const float* eb = sEG + (16 * j + n) * LDK;
+    for (int j = 0; j < 4; ++j) {   // tiles right of the diagonal come out masked to zero
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {   // rows of Kt (or Qt) against rows of Kh, 16 channels per step
+            const float* xa = (half == 0 ? sK : sQ) + (16 * w4 + n) * LDK;
+            const float* ea = sEG + (16 * w4 + n) * LDK;
+            const float* kb = sK + (16 * j + n) * LDK;
+            const float* eb = sEG + (16 * j + n) * LDK;
 #pragma unroll 4
-                for (int s = 0; s < DK / 16; ++s) {
-                    const int c0 = 16 * s + 4 * g;
-                    x = mma_bf16(to_bf16x4(ld4s(xa + c0) * ld4s(ea + c0)), to_bf16x4(ld4s(kb + c0) * rcp4(ld4s(eb + c0))), x);
-                }
-            } else if (half == 0) {
+            for (int s = 0; s < DK / 16; ++s) {
+                const int c0 = 16 * s + 4 * g;
+                x = mma_bf16(to_bf16x4(ld4s(xa + c0) * ld4s(ea + c0)), to_bf16x4(ld4s(kb + c0) * rcp4(ld4s(eb + c0))), x);
+            }
+        } else if (half == 0) {
 #pragma unroll 8
-                for (int s = 0; s < NKD; ++s) x = mma_f32(Kt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
+            for (int s = 0; s < NKD; ++s) x = mma_f32(Kt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
+        } else {
+#pragma unroll 8
+            for (int s = 0; s < NKD; ++s) x = mma_f32(Qt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w4 + 4 * g + e, jj = 16 * j + n;
+            if (half == 0) {
+                As[j][e] = jj < i ? x[e] : 0.f;
+                sT[i * LDC + jj] = jj < i ? sBeta[i] * x[e] : 0.f;
             } else {
-#pragma unroll 8
-                for (int s = 0; s < NKD; ++s) x = mma_f32(Qt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
+                sP[i * LDC + jj] = jj <= i ? x[e] : 0.f;
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w4 + 4 * g + e, jj = 16 * j + n;
-                if (half == 0) {
-                    As[j][e] = jj < i ? x[e] : 0.f;
-                    sT[i * LDC + jj] = jj < i ? sBeta[i] * x[e] : 0.f;
-                } else {
-                    sP[i * LDC + jj] = jj <= i ? x[e] : 0.f;
-                }
-            }
-        } else if (half == 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sP[(16 * w4 + 4 * g + e) * LDC + 16 * j + n] = 0.f;
         }
     }
     __syncthreads();
@@ -617,7 +629,8 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const size_t ri = rowi(16 * w4 + 4 * g + e) * DV + col0 + n;
-            p.a[e] = (half == 0 || dop) ? to_f32(pa[ri]) : 0.f;
+            const float xa = to_f32(pa[ri]);   // loaded unconditionally (pa is never null)
+            p.a[e] = (half == 0 || dop) ? xa : 0.f;
             p.b[e] = to_f32(pb[ri]);
             p.c[e] = to_f32(pc[ri]);
         }
@@ -641,6 +654,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
         pre = fetch(vb + 1);
         __syncthreads();
+        f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
         if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
             f32x4 r;
 #pragma unroll
@@ -661,7 +675,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) sR[(16 * w4 + 4 * g + e) * LDB + n] = r[e];
-        } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g))
+        } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * w4 + 4 * g + e;
@@ -671,25 +685,6 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 sDO[i * LDB + n] = i < nvalid ? dy * sg : 0.f;
                 if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
             }
-        }
-        __syncthreads();
-        if (half == 0) {   // U = T diag(beta) R (T lower triangular)
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF) {   // 16-token k-blocks 0 .. w4
-                for (int s = 0; s <= w4; ++s) {
-                    const int j0 = 16 * s + 4 * g;
-                    const f32x4 bb = {sBeta[j0] * sR[j0 * LDB + n], sBeta[j0 + 1] * sR[(j0 + 1) * LDB + n],
-                                      sBeta[j0 + 2] * sR[(j0 + 2) * LDB + n], sBeta[j0 + 3] * sR[(j0 + 3) * LDB + n]};
-                    u = mma_bf16(to_bf16x4(ld4s(sT + (16 * w4 + n) * LDC + j0)), to_bf16x4(bb), u);
-                }
-            } else {
-                for (int s = 0; s < 4 * (w4 + 1); ++s)
-                    u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
-        } else {           // dU = Ke dS + P^T dO (P^T upper triangular)
-            f32x4 du = {0.f, 0.f, 0.f, 0.f};
             if constexpr (BF) {
                 const float* xa = sK + (16 * w4 + n) * LDK;
                 const float* ea = sEG + (16 * w4 + n) * LDK;
@@ -705,8 +700,28 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll 8
                 for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
             }
-            if constexpr (BF) {   // 16-token k-blocks w4 .. 3
-                for (int s = w4; s < 4; ++s) {
+        }
+        __syncthreads();
+        if (half == 0) {   // U = T diag(beta) R (T lower triangular)
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BF) {   // 16-token k-blocks 0 .. 3 (T's tiles above block w4 are zero)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int j0 = 16 * s + 4 * g;
+                    const f32x4 bb = {sBeta[j0] * sR[j0 * LDB + n], sBeta[j0 + 1] * sR[(j0 + 1) * LDB + n],
+                                      sBeta[j0 + 2] * sR[(j0 + 2) * LDB + n], sBeta[j0 + 3] * sR[(j0 + 3) * LDB + n]};
+                    u = mma_bf16(to_bf16x4(ld4s(sT + (16 * w4 + n) * LDC + j0)), to_bf16x4(bb), u);
+                }
+            } else {
+                for (int s = 0; s < 4 * (w4 + 1); ++s)
+                    u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
+        } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
+            if constexpr (BF) {   // 16-token k-blocks 0 .. 3 (P^T's tiles below block w4 are zero)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
                     const int j0 = 16 * s + 4 * g, ci = 16 * w4 + n;
                     const f32x4 ap = {sP[j0 * LDC + ci], sP[(j0 + 1) * LDC + ci], sP[(j0 + 2) * LDC + ci],
                                       sP[(j0 + 3) * LDC + ci]};
@@ -724,8 +739,9 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         __syncthreads();
         f32x4 dut = {0.f, 0.f, 0.f, 0.f};
         if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
-            if constexpr (BF) {   // 16-token k-blocks w4 .. 3
-                for (int s = w4; s < 4; ++s) {
+            if constexpr (BF) {   // 16-token k-blocks 0 .. 3 (T^T's tiles below block w4 are zero)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
                     const int j0 = 16 * s + 4 * g, ci = 16 * w4 + n;
                     const f32x4 at = {sT[j0 * LDC + ci], sT[(j0 + 1) * LDC + ci], sT[(j0 + 2) * LDC + ci],
                                       sT[(j0 + 3) * LDC + ci]};
@@ -743,11 +759,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
                 dbp[e] += dut[e] * sR[i * LDB + n];
             }
-        } else {           // dP += dO U^T (column tiles j <= w4)
+        } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
             const bf16x4 ao = to_bf16x4(ld4s(sDO + (16 * w4 + n) * LDB + 4 * g));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (j <= w4) {
+                {
                     if constexpr (BF) {
                         dMP[j] = mma_bf16(ao, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
                     } else {
@@ -765,11 +781,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = dut[e];
         }
         __syncthreads();
-        if (half == 0) {   // dM -= dU~ U^T (column tiles j <= w4)
+        if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
             const bf16x4 am = to_bf16x4(-ld4s(sDU + (16 * w4 + n) * LDB + 4 * g));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (j <= w4) {
+                {
                     if constexpr (BF) {
                         dMP[j] = mma_bf16(am, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
                     } else {
@@ -860,7 +876,9 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     // fp32 for every I/O type: dgamma takes differences of these products
     // (dKt Kt - dKh Kh), and bf16 operands here doubled its error
     {
-        for (int s = 0; s < 4 * (w4 + 1); ++s) {
+        for (int s4 = 0; s4 <= w4; ++s4)
+#pragma unroll
+        for (int s = 4 * s4; s < 4 * s4 + 4; ++s) {
             const float ap = sP[(16 * w4 + n) * LDC + 4 * s + g], aa = sT[(16 * w4 + n) * LDC + 4 * s + g];
 #pragma unroll
             for (int c2 = 0; c2 < NTH2; ++c2) {
@@ -869,7 +887,9 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 aK[c2] = mma_f32(aa, kh, aK[c2]);
             }
         }
-        for (int s = 4 * w4; s < NKC; ++s) {
+        for (int s4 = w4; s4 < 4; ++s4)
+#pragma unroll
+        for (int s = 4 * s4; s < 4 * s4 + 4; ++s) {
             const float ap = sP[(4 * s + g) * LDC + 16 * w4 + n], aa = sT[(4 * s + g) * LDC + 16 * w4 + n];
 #pragma unroll
             for (int c2 = 0; c2 < NTH2; ++c2) {
@@ -934,14 +954,15 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * w4 + 4 * g + e;
             if (i < nvalid) {
-                const float nk = sNk[i], nq = sNq[i];
+                const float nk = sNk[i], nq = sNq[i], rk = sRk[i], rq = sRq[i];
                 const float kdi = sXD[i] + sXD[2 * C + i], qdi = sXD[C + i] + sXD[3 * C + i];
                 const size_t ri = rowi(i) * DK;
 #pragma unroll
                 for (int c2 = 0; c2 < NTH2; ++c2) {
                     const int ch = 16 * (ct0 + c2) + n;
-                    const float dkx = nk < 1e-6f ? aK[c2][e] * 1e6f : (aK[c2][e] - sK[i * LDK + ch] * kdi) / nk;
-                    const float dqx = nq < 1e-6f ? aQ[c2][e] * 1e6f : (aQ[c2][e] - sQ[i * LDK + ch] * qdi) / nq;
+                    // rk = 1 / max(|k|, 1e-6): below the floor the normaliser is the constant 1e6
+                    const float dkx = (nk < 1e-6f ? aK[c2][e] : aK[c2][e] - sK[i * LDK + ch] * kdi) * rk;
+                    const float dqx = (nq < 1e-6f ? aQ[c2][e] : aQ[c2][e] - sQ[i * LDK + ch] * qdi) * rq;
                     dkp[ri + ch] = from_f32<E>(dkx);
                     dqp[ri + ch] = from_f32<E>(dqx);
                 }
