@@ -443,9 +443,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         qx[jj] = ld4(qp + r);
         lx[jj] = *reinterpret_cast<const f32x4*>(a.log_alpha + r);
     }
-    const float bv = a.beta[rowi(t % C)];   // every thread loads (clamped): no load under a branch
+    // no branch around the beta load: every thread loads the beta of token
+    // t % C (clamped) and stores it; the threads sharing a token store the same value
+    const float bv = a.beta[rowi(t % C)];
     for (int idx = t; idx < C * LDC; idx += NTH) sT[idx] = 0.f;   // T's upper tiles stay zero
-    if (t < C) sBeta[t] = t < nvalid ? bv : 0.f;
+    sBeta[t % C] = t % C < nvalid ? bv : 0.f;
 #pragma unroll
     for (int jj = 0; jj < NPC; ++jj) {
         const int idx = t + jj * NTH, i = idx / TPL, ch = (idx % TPL) * 4;

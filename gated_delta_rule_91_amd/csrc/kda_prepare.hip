@@ -168,7 +168,12 @@ __global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a)
         kv[i][0] = k2[0]; kv[i][1] = k2[1];
         vv[i][0] = v2[0]; vv[i][1] = v2[1];
     }
-    if (t < C) sBeta[t] = (t < nvalid) ? a.beta[row0 + (size_t)(t < nvalid ? t : nvalid - 1) * H] : 0.f;
+    {   // no branch around the load: every thread loads the beta of token t % C
+        // (clamped) and stores it; the threads sharing a token store the same value
+        const int tb = t % C;
+        const float bv = a.beta[row0 + (size_t)(tb < nvalid ? tb : nvalid - 1) * H];
+        sBeta[tb] = (tb < nvalid) ? bv : 0.f;
+    }
     // inclusive cumulative log-decay inside the group
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
