@@ -15,7 +15,8 @@
 // rows x 4-column block of S in registers between the read and the write.
 // The state streams with non-temporal loads/stores (it is larger than the
 // last-level cache), and the column partial sums of p and r are combined
-// across row groups through LDS.
+// across row groups through LDS.  Residency is capped at two workgroups per
+// CU (see the launch).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -105,11 +106,17 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
     }
 }
 
+// LDS reserved (and unused) per workgroup so that at most two workgroups
+// share a CU: fewer state streams in flight at once run faster.  Measured at
+// 256 sequences x 32 heads, d = 128: 177-179 us per step with two per CU,
+// 189 us with three, 192 us with four (the register limit), 210 us with one.
+constexpr unsigned kDecodeLdsReserve = 64 * 1024;
+
 template <typename E, int DK>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     const int64_t blocks = a.N * (int64_t)a.H;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((kda_decode_kernel<E, DK>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((kda_decode_kernel<E, DK>), dim3((unsigned)blocks), dim3(kThreads), kDecodeLdsReserve, s, a);
     return hipGetLastError();
 }
 
