@@ -57,6 +57,8 @@ PATH_BYTES = 4 * D * 2 + D * 4 + 4 + D * 2          # q,k,v,g in; log_alpha, bet
 CARD_BYTES = 74240 // C    # update card per token-head (bf16, d=128; meaningful bytes, 1 KB padding excluded) -> 1,160
 PREP_BYTES = 3 * D * 2 + D * 4 + 4 + CARD_BYTES       # q,k,v,log_alpha,beta in; card out -> 2,444
 SCAN_BYTES = CARD_BYTES + D * 2 + D * 2               # card, g in; out -> 1,672
+# the card parts a segment summary reads: Wk, Ke^T, Wv (C x d bf16 each) and e^gamma_C (d fp32) -> 776
+SUMMARY_CARD_BYTES = (3 * C * D * 2 + D * 4) // C
 # algorithmic FLOPs per token-head of the chunk method (triangular C x C products at half):
 FLOP_TOK = 6 * D * D + C * (3 * D + 2 * D) + C * C / 3
 # decode: per (sequence, head) the fp32 state is read and written once, plus the token's inputs/outputs
@@ -363,10 +365,10 @@ def main():
             "workload": Ws["name"], "ms": total, "tokens_per_s": Bs * Ts_all / (total * 1e-3),
             "ms_per_call": times,
             # algorithmic bytes: prepare and scan as in the prefill; the
-            # summaries read the cards (1,160 B per token-head) and write
-            # 2 d^2 fp32 per segment-head; the combine reads and writes those
+            # summaries read Wk, Ke^T, Wv and e^gamma_C of the cards (776 B
+            # per token-head) and write 2 d^2 fp32 per segment-head
             "GBps": {"prepare": PREP_BYTES * ths / (times["prepare"] * 1e-3) / 1e9,
-                     "summarize": (CARD_BYTES * ths + 2 * D * D * 4 * Bs * nseg * Hs)
+                     "summarize": (SUMMARY_CARD_BYTES * ths + 2 * D * D * 4 * Bs * nseg * Hs)
                      / (times["summarize"] * 1e-3) / 1e9,
                      "scan": SCAN_BYTES * ths / (times["scan"] * 1e-3) / 1e9},
         }
