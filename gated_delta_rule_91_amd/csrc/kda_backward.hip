@@ -56,6 +56,20 @@ __device__ __forceinline__ f32x4 mma_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
     return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
 }
+// bf16 16x16x32 (the same matrix-pipe cycles as 16x16x16 for twice the
+// work): lane (n, g) supplies A[n][8g..8g+7] and B[8g..8g+7][n]
+__device__ __forceinline__ f32x4 mma_bf16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x4 lo, f32x4 hi) {
+    return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                  (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+}
+// eight consecutive rows of one column of an fp32 LDS tile (row stride ld)
+__device__ __forceinline__ bf16x8 col8(const float* p, int ld) {
+    return bf16x8{(__bf16)p[0], (__bf16)p[ld], (__bf16)p[2 * ld], (__bf16)p[3 * ld],
+                  (__bf16)p[4 * ld], (__bf16)p[5 * ld], (__bf16)p[6 * ld], (__bf16)p[7 * ld]};
+}
 __device__ __forceinline__ f32x4 ld4s(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 rcp4(f32x4 x) {
     return f32x4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
@@ -513,15 +527,17 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll
     for (int j = 0; j < 4; ++j) {   // tiles right of the diagonal come out masked to zero
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BF) {   // rows of Kt (or Qt) against rows of Kh, 16 channels per step
+        if constexpr (BF) {   // rows of Kt (or Qt) against rows of Kh, 32 channels per step
             const float* xa = (half == 0 ? sK : sQ) + (16 * w4 + n) * LDK;
             const float* ea = sEG + (16 * w4 + n) * LDK;
             const float* kb = sK + (16 * j + n) * LDK;
             const float* eb = sEG + (16 * j + n) * LDK;
-#pragma unroll 4
-            for (int s = 0; s < DK / 16; ++s) {
-                const int c0 = 16 * s + 4 * g;
-                x = mma_bf16(to_bf16x4(ld4s(xa + c0) * ld4s(ea + c0)), to_bf16x4(ld4s(kb + c0) * rcp4(ld4s(eb + c0))), x);
+#pragma unroll
+            for (int s = 0; s < DK / 32; ++s) {
+                const int c0 = 32 * s + 8 * g;
+                x = mma_bf16x32(to_bf16x8(ld4s(xa + c0) * ld4s(ea + c0), ld4s(xa + c0 + 4) * ld4s(ea + c0 + 4)),
+                                to_bf16x8(ld4s(kb + c0) * rcp4(ld4s(eb + c0)), ld4s(kb + c0 + 4) * rcp4(ld4s(eb + c0 + 4))),
+                                x);
             }
         } else if (half == 0) {
 #pragma unroll 8
@@ -664,12 +680,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             if constexpr (BF) {
                 const float* xa = sK + (16 * w4 + n) * LDK;
                 const float* ea = sEG + (16 * w4 + n) * LDK;
-#pragma unroll 4
-                for (int s = 0; s < DK / 16; ++s) {
-                    const int c0 = 16 * s + 4 * g;
-                    const f32x4 bs = {sS0[c0 * LDSB + n], sS0[(c0 + 1) * LDSB + n], sS0[(c0 + 2) * LDSB + n],
-                                      sS0[(c0 + 3) * LDSB + n]};
-                    r = mma_bf16(to_bf16x4(-(ld4s(xa + c0) * ld4s(ea + c0))), to_bf16x4(bs), r);
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s) {
+                    const int c0 = 32 * s + 8 * g;
+                    r = mma_bf16x32(to_bf16x8(-(ld4s(xa + c0) * ld4s(ea + c0)), -(ld4s(xa + c0 + 4) * ld4s(ea + c0 + 4))),
+                                    col8(sS0 + c0 * LDSB + n, LDSB), r);
                 }
             } else {
 #pragma unroll 8
@@ -691,12 +706,12 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 const float* xa = sK + (16 * w4 + n) * LDK;
                 const float* ea = sEG + (16 * w4 + n) * LDK;
                 const float* ec = sEG + (C - 1) * LDK;
-#pragma unroll 4
-                for (int s = 0; s < DK / 16; ++s) {
-                    const int c0 = 16 * s + 4 * g;
-                    const f32x4 bs = {sDS[c0 * LDSB + n], sDS[(c0 + 1) * LDSB + n], sDS[(c0 + 2) * LDSB + n],
-                                      sDS[(c0 + 3) * LDSB + n]};
-                    du = mma_bf16(to_bf16x4(ld4s(xa + c0) * rcp4(ld4s(ea + c0)) * ld4s(ec + c0)), to_bf16x4(bs), du);
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s) {
+                    const int c0 = 32 * s + 8 * g;
+                    du = mma_bf16x32(to_bf16x8(ld4s(xa + c0) * rcp4(ld4s(ea + c0)) * ld4s(ec + c0),
+                                               ld4s(xa + c0 + 4) * rcp4(ld4s(ea + c0 + 4)) * ld4s(ec + c0 + 4)),
+                                     col8(sDS + c0 * LDSB + n, LDSB), du);
                 }
             } else {
 #pragma unroll 8
@@ -706,13 +721,15 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         __syncthreads();
         if (half == 0) {   // U = T diag(beta) R (T lower triangular)
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF) {   // 16-token k-blocks 0 .. 3 (T's tiles above block w4 are zero)
+            if constexpr (BF) {   // 32-token k-blocks 0, 1 (T's tiles above block w4 are zero)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int j0 = 16 * s + 4 * g;
-                    const f32x4 bb = {sBeta[j0] * sR[j0 * LDB + n], sBeta[j0 + 1] * sR[(j0 + 1) * LDB + n],
-                                      sBeta[j0 + 2] * sR[(j0 + 2) * LDB + n], sBeta[j0 + 3] * sR[(j0 + 3) * LDB + n]};
-                    u = mma_bf16(to_bf16x4(ld4s(sT + (16 * w4 + n) * LDC + j0)), to_bf16x4(bb), u);
+                for (int s = 0; s < 2; ++s) {
+                    const int j0 = 32 * s + 8 * g;
+                    bf16x8 bb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bb[e] = (__bf16)(sBeta[j0 + e] * sR[(j0 + e) * LDB + n]);
+                    const float* ta = sT + (16 * w4 + n) * LDC + j0;
+                    u = mma_bf16x32(to_bf16x8(ld4s(ta), ld4s(ta + 4)), bb, u);
                 }
             } else {
                 for (int s = 0; s < 4 * (w4 + 1); ++s)
@@ -721,15 +738,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll
             for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
         } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
-            if constexpr (BF) {   // 16-token k-blocks 0 .. 3 (P^T's tiles below block w4 are zero)
+            if constexpr (BF) {   // 32-token k-blocks 0, 1 (P^T's tiles below block w4 are zero)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int j0 = 16 * s + 4 * g, ci = 16 * w4 + n;
-                    const f32x4 ap = {sP[j0 * LDC + ci], sP[(j0 + 1) * LDC + ci], sP[(j0 + 2) * LDC + ci],
-                                      sP[(j0 + 3) * LDC + ci]};
-                    const f32x4 bd = {sDO[j0 * LDB + n], sDO[(j0 + 1) * LDB + n], sDO[(j0 + 2) * LDB + n],
-                                      sDO[(j0 + 3) * LDB + n]};
-                    du = mma_bf16(to_bf16x4(ap), to_bf16x4(bd), du);
+                for (int s = 0; s < 2; ++s) {
+                    const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
+                    du = mma_bf16x32(col8(sP + j0 * LDC + ci, LDC), col8(sDO + j0 * LDB + n, LDB), du);
                 }
             } else {
                 for (int s = 4 * w4; s < NKC; ++s)
@@ -741,15 +754,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         __syncthreads();
         f32x4 dut = {0.f, 0.f, 0.f, 0.f};
         if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
-            if constexpr (BF) {   // 16-token k-blocks 0 .. 3 (T^T's tiles below block w4 are zero)
+            if constexpr (BF) {   // 32-token k-blocks 0, 1 (T^T's tiles below block w4 are zero)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int j0 = 16 * s + 4 * g, ci = 16 * w4 + n;
-                    const f32x4 at = {sT[j0 * LDC + ci], sT[(j0 + 1) * LDC + ci], sT[(j0 + 2) * LDC + ci],
-                                      sT[(j0 + 3) * LDC + ci]};
-                    const f32x4 bd = {sDU[j0 * LDB + n], sDU[(j0 + 1) * LDB + n], sDU[(j0 + 2) * LDB + n],
-                                      sDU[(j0 + 3) * LDB + n]};
-                    dut = mma_bf16(to_bf16x4(at), to_bf16x4(bd), dut);
+                for (int s = 0; s < 2; ++s) {
+                    const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
+                    dut = mma_bf16x32(col8(sT + j0 * LDC + ci, LDC), col8(sDU + j0 * LDB + n, LDB), dut);
                 }
             } else {
                 for (int s = 4 * w4; s < NKC; ++s)
