@@ -654,6 +654,22 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         }
         return p;
     };
+    // the A operands that stay the same in every column block, as bf16
+    // fragments: -Kt rows 16 w4 .. for R on half 0, K_end rows for K_end dS on half 1
+    constexpr int NKF = BF ? DK / 32 : 1;
+    bf16x8 afr[NKF];
+    if constexpr (BF) {
+        const float* xa = sK + (16 * w4 + n) * LDK;
+        const float* ea = sEG + (16 * w4 + n) * LDK;
+        const float* ec = sEG + (C - 1) * LDK;
+#pragma unroll
+        for (int s = 0; s < NKF; ++s) {
+            const int c0 = 32 * s + 8 * g;
+            const f32x4 xl = ld4s(xa + c0), xh = ld4s(xa + c0 + 4), el = ld4s(ea + c0), eh = ld4s(ea + c0 + 4);
+            afr[s] = half == 0 ? to_bf16x8(-(xl * el), -(xh * eh))
+                               : to_bf16x8(xl * rcp4(el) * ld4s(ec + c0), xh * rcp4(eh) * ld4s(ec + c0 + 4));
+        }
+    }
     Pre pre = fetch(0);
     for (int vb = 0; vb < DV / NB; ++vb) {
         const int col0 = NB * vb;
@@ -678,14 +694,8 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
             if constexpr (BF) {
-                const float* xa = sK + (16 * w4 + n) * LDK;
-                const float* ea = sEG + (16 * w4 + n) * LDK;
 #pragma unroll
-                for (int s = 0; s < DK / 32; ++s) {
-                    const int c0 = 32 * s + 8 * g;
-                    r = mma_bf16x32(to_bf16x8(-(ld4s(xa + c0) * ld4s(ea + c0)), -(ld4s(xa + c0 + 4) * ld4s(ea + c0 + 4))),
-                                    col8(sS0 + c0 * LDSB + n, LDSB), r);
-                }
+                for (int s = 0; s < NKF; ++s) r = mma_bf16x32(afr[s], col8(sS0 + (32 * s + 8 * g) * LDSB + n, LDSB), r);
             } else {
 #pragma unroll 8
                 for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w4 + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
@@ -703,16 +713,8 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
             }
             if constexpr (BF) {
-                const float* xa = sK + (16 * w4 + n) * LDK;
-                const float* ea = sEG + (16 * w4 + n) * LDK;
-                const float* ec = sEG + (C - 1) * LDK;
 #pragma unroll
-                for (int s = 0; s < DK / 32; ++s) {
-                    const int c0 = 32 * s + 8 * g;
-                    du = mma_bf16x32(to_bf16x8(ld4s(xa + c0) * rcp4(ld4s(ea + c0)) * ld4s(ec + c0),
-                                               ld4s(xa + c0 + 4) * rcp4(ld4s(ea + c0 + 4)) * ld4s(ec + c0 + 4)),
-                                     col8(sDS + c0 * LDSB + n, LDSB), du);
-                }
+                for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], col8(sDS + (32 * s + 8 * g) * LDSB + n, LDSB), du);
             } else {
 #pragma unroll 8
                 for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
