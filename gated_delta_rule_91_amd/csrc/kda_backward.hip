@@ -121,18 +121,23 @@ __device__ __forceinline__ float frag_elem(float v, int) { return v; }
 __device__ __forceinline__ float frag_elem(bf16x8 v, int e) { return (float)v[e]; }
 
 // Visit an R x K matrix stored in A-fragment order: f(row, k, value) for
-// every element, each lane fragment read with one load.
+// every element, each lane fragment read with one load (a thread's loads are
+// all requested before the first is used).
 template <typename E, int R, int K, typename F>
 __device__ __forceinline__ void for_each_frag(const char* src, int t, F f) {
-    constexpr int KF = MM<E>::KF, KS = MM<E>::KS;
+    constexpr int KF = MM<E>::KF, KS = MM<E>::KS, NF = R * K / KF / kThreads;
+    static_assert((R * K / KF) % kThreads == 0, "whole fragments per thread");
     typedef typename MM<E>::frag Fr;
-    for (int idx = t; idx < R * K / KF; idx += kThreads) {
-        const int blk = idx >> 6, lane = idx & 63;
+    Fr v[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) v[j] = reinterpret_cast<const Fr*>(src)[t + j * kThreads];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        const int idx = t + j * kThreads, blk = idx >> 6, lane = idx & 63;
         const int row = 16 * (blk / (K / KS)) + (lane & 15);
         const int k = (blk % (K / KS)) * KS + (lane >> 4) * KF;
-        const Fr v = reinterpret_cast<const Fr*>(src)[idx];
 #pragma unroll
-        for (int e = 0; e < KF; ++e) f(row, k + e, frag_elem(v, e));
+        for (int e = 0; e < KF; ++e) f(row, k + e, frag_elem(v[j], e));
     }
 }
 
@@ -186,13 +191,25 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_card_kernel(BackwardArgs a) 
         const size_t row0 = ((size_t)b * T + tok0) * H + h;
         const E* dop = reinterpret_cast<const E*>(a.d_out);
         const E* gp = reinterpret_cast<const E*>(a.g);
-        for (int idx = t; idx < C * DV / 4; idx += kThreads) {
+        const E* dsrc = dop ? dop : gp;   // loaded unconditionally, zeroed after when d_out is absent
+        constexpr int NP = C * DV / 4 / kThreads;   // four-column pieces per thread
+        static_assert((C * DV / 4) % kThreads == 0, "whole pieces per thread");
+        f32x4 dl[NP], gg[NP];
+#pragma unroll
+        for (int jj = 0; jj < NP; ++jj) {   // every piece requested before the first is used
+            const int idx = t + jj * kThreads;
             const int i = idx / (DV / 4), v4 = (idx % (DV / 4)) * 4;
             const size_t r = (row0 + (size_t)(i < nvalid ? i : nvalid - 1) * H) * DV + v4;
-            const f32x4 dy = dop ? ld4(dop + r) : f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 gg = ld4(gp + r);
+            dl[jj] = ld4(dsrc + r);
+            gg[jj] = ld4(gp + r);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sDOT[(v4 + e) * LDC + i] = from_f32<E>(i < nvalid ? dy[e] * sigmoidf_(gg[e]) : 0.f);
+        for (int jj = 0; jj < NP; ++jj) {
+            const int idx = t + jj * kThreads;
+            const int i = idx / (DV / 4), v4 = (idx % (DV / 4)) * 4;
+            const f32x4 dy = dop ? dl[jj] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sDOT[(v4 + e) * LDC + i] = from_f32<E>(i < nvalid ? dy[e] * sigmoidf_(gg[jj][e]) : 0.f);
         }
     }
     if (t < DK) reinterpret_cast<float*>(bcard + BC::G)[t] = reinterpret_cast<const float*>(card + CL::GC)[t];
