@@ -77,8 +77,9 @@ struct PrepLds {
     static constexpr size_t BYTES = RK + (size_t)C * 4;
 };
 
+// two workgroups per CU with bf16 cards; the fp32 variant's LDS allows one
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads, 2) void kda_prepare_kernel(PrepareArgs a) {
+__global__ __launch_bounds__(kThreads, sizeof(E) == 2 ? 2 : 1) void kda_prepare_kernel(PrepareArgs a) {
     using M = MM<E>;
     using CL = Card<E, DK>;
     using LY = PrepLds<E, DK>;

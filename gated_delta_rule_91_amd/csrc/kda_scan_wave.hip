@@ -102,7 +102,6 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
     using CL = Card<__bf16, DK>;
     using WR = WaveRing<DK>;
     using R = WaveOps<SPW>;
-    constexpr int C = kChunk;
     constexpr int NKB = DK / 32;                   // key k-blocks (pairs of key tiles)
     constexpr int NT = DK / 16;                    // value-column slices
     constexpr int NTALL = 2 * NT;                  // + transition-column slices
