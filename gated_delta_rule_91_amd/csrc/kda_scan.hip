@@ -143,7 +143,7 @@ __device__ __forceinline__ void load_ops(ChunkOps<E, DK, NTW>& o, const char* ca
 // One workgroup = NTW adjacent 16-column slices of one (batch row, head):
 // the card fragments a wave loads serve all NTW slices.
 // Depth of the operand ring (chunks of card fragments in flight per wave):
-// four, or three for four or more slices per workgroup (register file), and how far
+// four, or three for four or more slices per workgroup, or two for fp32 at d_k = 128 (register file), and how far
 // past the chunk a ring load fetches the L2 prefetch runs.
 constexpr int kRing4 = 4;
 constexpr int kPrefetch = kRing4 + 1;
@@ -356,8 +356,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     // load-counter waits stay exact.  It runs over full chunks only; the
     // rest (fewer than kRing full chunks, then a partial one) finish in the
     // tail from the slots already loaded.  (Named ring slots: an array of
-    // them allocates worse.)
-    constexpr int kRing = NTW >= 4 ? 3 : kRing4;
+    // them allocates worse.)  fp32 operands at d_k = 128 take twice the
+    // registers per chunk: a two-deep ring keeps them out of scratch memory
+    // (measured 1.96 -> 0.48 ms on 8K tokens x 32 heads with one slice per
+    // workgroup, 1.55 -> 0.39 ms with two, 1.61 -> 0.80 ms with four).
+    constexpr int kRing = (sizeof(E) == 4 && DK == 128) ? 2 : (NTW >= 4 ? 3 : kRing4);
     static_assert(kRing >= 2 && kRing <= 4, "ring depth");
     if (NC > 0) {
         using Full = std::integral_constant<bool, true>;
