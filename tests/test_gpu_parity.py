@@ -115,11 +115,14 @@ def test_bf16_prefill_vs_oracle(dk, T, H, mu):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
-def test_f32_d128_prefill_vs_oracle():
-    """fp32 at d = 128 with 64 (row, head) chains: two 16-column slices per
-    workgroup in the hand-off, ragged last chunk."""
-    note("[f32 prefill] dk=128 B=2 T=100 H=32")
-    inp = make_inputs(2, 100, 32, 128, 128, io_dtype="f32", seed=23, alpha_min=0.9, logit_mu=-2.0, with_state0=True)
+# fp32 at d = 128 runs a two-deep operand ring: 8 (row, head) chains give one
+# 16-column slice per workgroup (odd and even chunk counts, full and ragged
+# last chunk), 64 chains two slices, 256 chains four
+@pytest.mark.parametrize("B,T,H", [(2, 100, 32), (1, 300, 8), (1, 256, 8), (1, 129, 8), (4, 200, 64)])
+def test_f32_d128_prefill_vs_oracle(B, T, H):
+    note(f"[f32 prefill] dk=128 B={B} T={T} H={H}")
+    inp = make_inputs(B, T, H, 128, 128, io_dtype="f32", seed=23 + T, alpha_min=0.9, logit_mu=-2.0,
+                      with_state0=True)
     d = kda.to_device(inp)
     out, st = gpu_prefill(d, inp.log_alpha_min)
     o_ref, s_ref = oracle_run(inp)
