@@ -384,10 +384,10 @@ struct GradLds {
     static constexpr size_t EG = Q + (size_t)C * LDK * 4;   // e^gamma
     static constexpr size_t P = EG + (size_t)C * LDK * 4;   // P, then dP, then dgamma (spans P and T)
     static constexpr size_t T = P + (size_t)C * LDC * 4;    // diag(beta) A -> T, then dA
-    static constexpr size_t R = T + (size_t)C * LDC * 4;
+    static constexpr size_t R = T + (size_t)C * LDC * 4;      // R, then dU~
     static constexpr size_t U = R + (size_t)C * LDB * 4;
     static constexpr size_t DO = U + (size_t)C * LDB * 4;
-    static constexpr size_t DU = DO + (size_t)C * LDB * 4;  // dU, then dU~
+    static constexpr size_t DU = DO + (size_t)C * LDB * 4;  // dU
     static constexpr size_t BETA = DU + (size_t)C * LDB * 4;
     static constexpr size_t NK = BETA + (size_t)C * 4;      // |k|
     static constexpr size_t NQ = NK + (size_t)C * 4;        // |q|
@@ -784,10 +784,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w4 + n], sDU[(4 * s + g) * LDB + n], dut);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 4; ++e) {   // dU~ replaces R in LDS (each element by the lane that read it)
                 const int i = 16 * w4 + 4 * g + e;
                 if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
                 dbp[e] += dut[e] * sR[i * LDB + n];
+                sR[i * LDB + n] = dut[e];
             }
         } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
             const bf16x4 ao = to_bf16x4(ld4s(sDO + (16 * w4 + n) * LDB + 4 * g));
@@ -806,13 +807,8 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             }
         }
         __syncthreads();
-        if (half == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = dut[e];
-        }
-        __syncthreads();
         if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
-            const bf16x4 am = to_bf16x4(-ld4s(sDU + (16 * w4 + n) * LDB + 4 * g));
+            const bf16x4 am = to_bf16x4(-ld4s(sR + (16 * w4 + n) * LDB + 4 * g));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 {
@@ -821,7 +817,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     } else {
 #pragma unroll
                         for (int s = 0; s < NB / 4; ++s)
-                            dMP[j] = mma_f32(-sDU[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
+                            dMP[j] = mma_f32(-sR[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
                                              dMP[j]);
                     }
                 }
@@ -831,7 +827,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         if constexpr (BF) {   // the block's 16 value columns are one bf16 k-step
             const int ra = (16 * w4 + n) * LDB + 4 * g;
             const bf16x4 ao = to_bf16x4(ld4s(sDO + ra));
-            const bf16x4 ar = to_bf16x4(-sBeta[16 * w4 + n] * ld4s(sDU + ra));
+            const bf16x4 ar = to_bf16x4(-sBeta[16 * w4 + n] * ld4s(sR + ra));
             const bf16x4 au = to_bf16x4(ld4s(sU + ra));
 #pragma unroll
             for (int c2 = 0; c2 < NTH2; ++c2) {
@@ -845,7 +841,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll
         for (int s = 0; s < NB / 4; ++s) {
             const float ao = sDO[(16 * w4 + n) * LDB + 4 * s + g];
-            const float ar = -sBeta[16 * w4 + n] * sDU[(16 * w4 + n) * LDB + 4 * s + g];
+            const float ar = -sBeta[16 * w4 + n] * sR[(16 * w4 + n) * LDB + 4 * s + g];
             const float au = sU[(16 * w4 + n) * LDB + 4 * s + g];
 #pragma unroll
             for (int c2 = 0; c2 < NTH2; ++c2) {
