@@ -376,13 +376,25 @@ __global__ __launch_bounds__(kThreads, sizeof(E) == 2 ? 2 : 1) void kda_prepare_
         __syncthreads();
     }
     // D3: M = T diag(beta) -> MFMA operand type, zero above the diagonal
-    for (int idx = t; idx < C * C / 4; idx += kThreads) {
-        const int row = idx / (C / 4), col = (idx % (C / 4)) * 4;
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(sBeta + col);
-        f32x4 x;
+    // (a thread's LDS reads all issued before its writes)
+    {
+        constexpr int ND = C * C / 4 / kThreads;
+        static_assert((C * C / 4) % kThreads == 0 && LDA % 4 == 0, "whole 4-element pieces");
+        f32x4 av[ND], bt[ND];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (col + e <= row) ? sA[row * LDA + col + e] * bt[e] : 0.f;
-        st4(sTb + row * LDT + col, x);
+        for (int j = 0; j < ND; ++j) {
+            const int idx = t + j * kThreads, row = idx / (C / 4), col = (idx % (C / 4)) * 4;
+            av[j] = *reinterpret_cast<const f32x4*>(sA + row * LDA + col);
+            bt[j] = *reinterpret_cast<const f32x4*>(sBeta + col);
+        }
+#pragma unroll
+        for (int j = 0; j < ND; ++j) {
+            const int idx = t + j * kThreads, row = idx / (C / 4), col = (idx % (C / 4)) * 4;
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (col + e <= row) ? av[j][e] * bt[j][e] : 0.f;
+            st4(sTb + row * LDT + col, x);
+        }
     }
     __syncthreads();
 
