@@ -1,6 +1,6 @@
 // kda_scan_wave.hip -- the segment summaries of the context-parallel scheme
 // [zuoshipin.com/article/18261 §三, "KDA 上下文并行" paragraph] with one
-// 16-column slice of the augmented state per wave (bf16 cards): the hand-off
+// or two 16-column slices of the augmented state per wave (bf16 cards): the hand-off
 // of [Bz | A] from [0 | I] over a segment's cards, with the same per-chunk
 // arithmetic as kda_scan_kernel [same page, §四, FlashKDA paragraph: only the
 // hand-off stays sequential]:
@@ -31,8 +31,6 @@
 // there.  1 KB fragment blocks are stored 64 bytes apart so that the gathered
 // row reads do not collide in LDS banks.  The Wv rows of a wave's slices come
 // through a small register ring.
-#include <type_traits>
-
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -48,7 +46,6 @@ constexpr int kBlkPitch = 1024 + 64;                   // LDS bytes per 1 KB fra
 constexpr int kPullAheadW = 1;                         // L2 pull: chunks past the last ring load
 
 typedef __attribute__((address_space(3))) char lds_c;
-typedef __bf16 bf16x8_ __attribute__((ext_vector_type(8)));
 
 template <int DK>
 struct WaveRing {
@@ -73,18 +70,18 @@ __device__ __forceinline__ uint32_t frag_at(int b0, int nkb, int r, int kb, int 
     return (uint32_t)(blk * kBlkPitch + (g * 16 + (r & 15)) * 16);
 }
 
-__device__ __forceinline__ bf16x8_ ld_lds8(const lds_c* base, uint32_t off) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_*>(base + off);
+__device__ __forceinline__ bf16x8 ld_lds8(const lds_c* base, uint32_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(base + off);
 }
 __device__ __forceinline__ f32x4 ld_lds4f(const lds_c* base, uint32_t off) {
     return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(base + off);
 }
-__device__ __forceinline__ f32x4 mma16(bf16x8_ a, bf16x8_ b, f32x4 c) {
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 // the B fragment of k-block p from the accumulator pair (2p, 2p+1)
-__device__ __forceinline__ bf16x8_ pack_pair(f32x4 lo, f32x4 hi) {
-    return bf16x8_{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+__device__ __forceinline__ bf16x8 pack_pair(f32x4 lo, f32x4 hi) {
+    return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
                    (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
 }
 
@@ -264,7 +261,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
         const lds_c* sl = ring_l + (size_t)(c % WR::SLOTS) * WR::SLOT;
 
         // X (entering the chunk) as bf16 B fragments of Wk X
-        bf16x8_ xF[SPW][NKB];
+        bf16x8 xF[SPW][NKB];
 #pragma unroll
         for (int s = 0; s < SPW; ++s)
 #pragma unroll
@@ -278,7 +275,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
             for (int hh = 0; hh < 2; ++hh) {
                 // A: Wk rows tau(m) = 32q + 8(m/4) + 4hh + m%4 for this lane's m = n
                 const int tau = 32 * q + 8 * (n >> 2) + 4 * hh + (n & 3);
-                bf16x8_ wk[NKB];
+                bf16x8 wk[NKB];
 #pragma unroll
                 for (int p = 0; p < NKB; ++p) wk[p] = ld_lds8(sl, frag_at(WR::B_WK, NKB, tau, p, g));
 #pragma unroll
@@ -291,7 +288,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
                     U[s][q][hh] = -acc;
                 }
             }
-        bf16x8_ uF[SPW][2];   // U as B operand (token k-block q)
+        bf16x8 uF[SPW][2];   // U as B operand (token k-block q)
 #pragma unroll
         for (int s = 0; s < SPW; ++s)
 #pragma unroll
@@ -304,8 +301,8 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
             for (int hh = 0; hh < 2; ++hh) {
                 const f32x4 gc = ld_lds4f(sl, (uint32_t)(WR::GC_OFF + (32 * p + 8 * g + 4 * hh) * 4));
                 const int kap = 32 * p + 8 * (n >> 2) + 4 * hh + (n & 3);
-                const bf16x8_ ke0 = ld_lds8(sl, frag_at(WR::B_KE, 2, kap, 0, g));
-                const bf16x8_ ke1 = ld_lds8(sl, frag_at(WR::B_KE, 2, kap, 1, g));
+                const bf16x8 ke0 = ld_lds8(sl, frag_at(WR::B_KE, 2, kap, 0, g));
+                const bf16x8 ke1 = ld_lds8(sl, frag_at(WR::B_KE, 2, kap, 1, g));
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) {
                     f32x4 acc = X[s][p][hh] * gc;
