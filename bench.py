@@ -1,7 +1,7 @@
 """KDA benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-segmented] [--no-backward]
-                    [--no-cpu-baseline]
+                    [--no-varlen] [--no-pipelined] [--no-cpu-baseline]
 
 A step is one chunked prefill (update-card preparation + ordered hand-off
 with the gated read-out) of the long-prefill workload: B=1, T=65,536, H=32,
@@ -26,6 +26,9 @@ Also reported on the same JSON line:
     (kda_chunk_scan_checkpoints), beside the plain scan, and the last 4,096
     tokens prefilled again from the checkpoint cached before them (the
     prefix-cache use: prepare + scan with state_in);
+  * the same step through kda_prefill_pipelined: chunk ranges of 128 or 256
+    chunks, each range's prepare on a second stream overlapping the previous
+    range's scan, with two ranges' cards instead of the whole sequence's;
   * packed variable-length prefill: the long workload's 65,536 tokens x 32
     heads re-cut into sequences of a seeded length mix (kda_varlen_prepare +
     kda_varlen_scan), tokens/s beside the uniform step;
@@ -105,6 +108,7 @@ def main():
     ap.add_argument("--no-segmented", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-pipelined", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -256,7 +260,36 @@ def main():
                                         f"{T - new_t} tokens",
                             "ms": res_ms, "tokens_per_s": B * new_t / (res_ms * 1e-3),
                             "identical_to_uninterrupted": same}
-        del d, ws, out, st, ck, sl, s_cached, ws_r, out_r, st_r
+        del ck, sl, s_cached, ws_r, out_r, st_r
+        # the same step as chunk ranges, each range's prepare on a second
+        # stream overlapping the previous range's scan (two ranges' cards)
+        if not args.no_pipelined:
+            pipe = {}
+            out_p = torch.empty_like(out)
+            st_p = torch.empty_like(st)
+            for rc in (128, 256):
+                ws_p = torch.empty(kda.pipelined_workspace_size(p, rc), dtype=torch.uint8, device=dev)
+
+                def pstep():
+                    kda.prefill_pipelined(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["g"], floor,
+                                          out=out_p, state_out=st_p, range_chunks=rc, workspace=ws_p)
+
+                pstep()
+                torch.cuda.synchronize()
+                same = bool(torch.equal(out_p, out) and torch.equal(st_p, st))
+                e0.record(stream)
+                for _ in range(10):
+                    pstep()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                pms = e0.elapsed_time(e1) / 10
+                log(f"[bench] pipelined, ranges of {rc} chunks: {pms:.3f} ms (identical to the step: {same})")
+                pipe[str(rc)] = {"ms": pms, "workspace_bytes": ws_p.numel(), "identical_to_step": same}
+                del ws_p
+            result["pipelined"] = {"workload": W["name"], "step_ms": ms, "card_workspace_bytes": ws.numel(),
+                                   "by_range_chunks": pipe}
+            del out_p, st_p
+        del d, ws, out, st
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode

@@ -9,8 +9,10 @@ CPU or PyTorch fallback: if the library is missing, every call raises.
 Entry points (same names as the C ABI, minus the ``kda_`` prefix):
     workspace_size, chunk_prepare, chunk_scan, chunk_scan_checkpoints, segment_summarize,
     segment_combine, decode_step, backward_workspace_size, backward,
-    varlen_workspace_size, varlen_prepare, varlen_scan
+    varlen_workspace_size, varlen_prepare, varlen_scan, pipelined_workspace_size
 Conveniences built from them: prefill, segmented_prefill, varlen_prefill.
+prefill_pipelined calls kda_prefill_pipelined (chunk ranges, the next range's
+cards prepared on a second stream during the current range's scan);
 prefill_noalloc calls kda_prefill_noalloc, which needs no workspace.
 """
 from __future__ import annotations
@@ -30,8 +32,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "w
 EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_chunk_scan_checkpoints",
            "kda_segment_summarize",
            "kda_segment_combine", "kda_decode_step", "kda_backward_workspace_size", "kda_backward",
-           "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan", "kda_prefill_noalloc",
-           "kda_status_string")
+           "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan",
+           "kda_pipelined_workspace_size", "kda_prefill_pipelined", "kda_prefill_noalloc", "kda_status_string")
 # bytes of kda_prefill_noalloc's fixed per-GPU scratch area (KDA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -75,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.kda_varlen_workspace_size.restype = SZ
         L.kda_varlen_prepare.argtypes = [PP, I64, P, P, P, P, P, P, P, SZ, P]
         L.kda_varlen_scan.argtypes = [PP, I64, P, P, SZ, P, P, P, P, P]
+        L.kda_pipelined_workspace_size.argtypes = [PP, I32]
+        L.kda_pipelined_workspace_size.restype = SZ
+        L.kda_prefill_pipelined.argtypes = [PP, P, P, P, P, P, P, P, P, P, I32, P, SZ, P, P]
         L.kda_prefill_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P]
         for f in EXPORTS[1:-1]:
             if not f.endswith("workspace_size"):
@@ -395,6 +400,66 @@ def prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, wo
     """Chunked prefill: prepare + scan.  Returns (out, final state)."""
     ws = chunk_prepare(q, k, v, log_alpha, beta, log_alpha_min, workspace=workspace, stream=stream)
     return chunk_scan(ws, g, log_alpha_min, state_in=state_in, stream=stream)
+
+
+def pipelined_workspace_size(p: KdaProblem, range_chunks: int) -> int:
+    n = lib().kda_pipelined_workspace_size(ctypes.byref(p), _range_chunks(range_chunks))
+    if n == 0 and p.batch * p.heads > 0:
+        raise KdaError("kda_pipelined_workspace_size", 2)
+    return n
+
+
+def _range_chunks(range_chunks) -> int:
+    if not isinstance(range_chunks, int) or not 1 <= range_chunks <= 2 ** 31 - 1:
+        raise ValueError(f"range_chunks must be an int in [1, 2**31 - 1], got {range_chunks!r}")
+    return range_chunks
+
+
+_AUX_STREAMS = {}
+
+
+def _aux_stream(device):
+    """A second stream per device (default priority) for the pipelined prefill."""
+    torch = _torch()
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    if idx not in _AUX_STREAMS:
+        _AUX_STREAMS[idx] = torch.cuda.Stream(device=idx)
+    return _AUX_STREAMS[idx]
+
+
+def prefill_pipelined(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, out=None, state_out=None,
+                      want_state: bool = True, range_chunks: int = 256, workspace=None, stream=None,
+                      aux_stream=None):
+    """Chunked prefill in ranges of range_chunks chunks through
+    kda_prefill_pipelined: the next range's cards are prepared on aux_stream
+    (a cached second stream unless given) while the current range is scanned
+    on `stream`.  The workspace holds two ranges' cards and the carried state
+    (allocated here unless given).  Returns (out, state_out)."""
+    torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_in", state_in, (B, H, dk, dv), torch.float32, q.device)
+    _expect("out", out, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_out", state_out, (B, H, dk, dv), torch.float32, q.device)
+    p = _problem_of(q, v, log_alpha_min)
+    rc = _range_chunks(range_chunks)
+    need = pipelined_workspace_size(p, rc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device)
+    if out is None:
+        out = torch.empty_like(g)
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    aux = aux_stream if aux_stream is not None else _aux_stream(q.device)
+    _check("kda_prefill_pipelined", lib().kda_prefill_pipelined(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g), _ptr(state_in),
+        _ptr(out), _ptr(state_out), rc, _ptr(workspace), workspace.numel(), _stream(stream, q.device),
+        aux.cuda_stream))
+    return out, state_out
 
 
 def prefill_noalloc(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, out=None, state_out=None,

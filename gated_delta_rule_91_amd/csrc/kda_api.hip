@@ -103,6 +103,58 @@ kda_status check_varlen(const kda_problem* p, int64_t n_seq) {
     return KDA_OK;
 }
 
+// Launch arguments for chunks [c0, c1) of every (row, head) of a uniform
+// batch: the range's first token rows inside the whole [B, T, H, d] arrays
+// (rows stay T tokens apart), its cards at `cards`.  The caller sets the
+// scan's state_in and state_out.
+struct RangeLaunch {
+    PrepareArgs pa;
+    ScanArgs sa;
+};
+RangeLaunch range_launch(const kda_problem* p, const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const void* g, void* out, char* cards, int64_t c0, int64_t c1) {
+    const size_t esz = p->io_dtype == KDA_BF16 ? 2 : 4;
+    const int64_t T = p->seqlen;
+    const int64_t t0 = c0 * p->chunk, t1 = c1 * p->chunk < T ? c1 * p->chunk : T;
+    const size_t tok = (size_t)t0 * (size_t)p->heads;   // row-0 offset of the range, in token-heads
+    RangeLaunch r = {};
+    r.pa.q = static_cast<const char*>(q) + tok * p->dk * esz;
+    r.pa.k = static_cast<const char*>(k) + tok * p->dk * esz;
+    r.pa.v = static_cast<const char*>(v) + tok * p->dv * esz;
+    r.pa.log_alpha = log_alpha + tok * p->dk;
+    r.pa.beta = beta + tok;
+    r.pa.ws = cards;
+    r.pa.B = p->batch; r.pa.T = t1 - t0; r.pa.row_stride = T; r.pa.H = p->heads; r.pa.NC = (int)(c1 - c0);
+    r.pa.floor_ = p->log_alpha_min;
+    r.sa.ws = cards;
+    r.sa.g = static_cast<const char*>(g) + tok * p->dv * esz;
+    r.sa.out = static_cast<char*>(out) + tok * p->dv * esz;
+    r.sa.B = p->batch; r.sa.T = t1 - t0; r.sa.row_stride = T; r.sa.H = p->heads; r.sa.NC = (int)(c1 - c0);
+    return r;
+}
+
+// No tokens: state_out = state_in (or zero), through the scan kernel.
+kda_status copy_state(const kda_problem* p, const float* state_in, float* state_out, hipStream_t s) {
+    ScanArgs a = {};
+    a.state_in = state_in; a.state_out = state_out;
+    a.B = p->batch; a.T = 0; a.H = p->heads; a.NC = 0;
+    return hip_status(launch_scan(p->io_dtype == KDA_BF16, p->dk, false, a, s));
+}
+
+// The pipelined prefill's workspace: the carried state, then one or two
+// ranges' cards.
+size_t state_bytes_of(const kda_problem* p) {
+    return ((size_t)p->batch * (size_t)p->heads * (size_t)p->dk * (size_t)p->dv * 4 + 255) / 256 * 256;
+}
+int64_t range_of(const kda_problem* p, int32_t range_chunks) {
+    const int64_t nc = n_chunks(p);
+    return range_chunks < nc ? range_chunks : nc;
+}
+size_t range_card_bytes(const kda_problem* p, int64_t rc) {
+    return ((size_t)rc * (size_t)p->batch * (size_t)p->heads * card_bytes(p->io_dtype == KDA_BF16, p->dk) + 255) /
+           256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +376,74 @@ kda_status kda_backward(const kda_problem* p, const void* q, const void* k, cons
     return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, (hipStream_t)stream));
 }
 
+size_t kda_pipelined_workspace_size(const kda_problem* p, int32_t range_chunks) {
+    if (check_problem(p) != KDA_OK || range_chunks < 1) return 0;
+    const int64_t rc = range_of(p, range_chunks);
+    const int nbuf = n_chunks(p) > rc ? 2 : 1;
+    return state_bytes_of(p) + (size_t)nbuf * range_card_bytes(p, rc);
+}
+
+kda_status kda_prefill_pipelined(const kda_problem* p, const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta, const void* g, const float* state_in,
+                                 void* out, float* state_out, int32_t range_chunks, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* aux_stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    if (range_chunks < 1) return KDA_ERR_INVALID_ARGUMENT;
+    const bool tokens = p->batch > 0 && p->seqlen > 0;
+    if (!ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) || !ok_ptr(log_alpha, tokens) ||
+        !ok_beta(beta, tokens) || !ok_ptr(g, tokens) || !ok_ptr(out, tokens) || !ok_ptr(workspace, tokens) ||
+        !ok_opt_ptr(state_in) || !ok_opt_ptr(state_out))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_pipelined_workspace_size(p, range_chunks)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (p->batch == 0 || (!tokens && !state_out)) return KDA_OK;
+    hipStream_t s = (hipStream_t)stream, aux = (hipStream_t)aux_stream;
+    const bool bf16 = p->io_dtype == KDA_BF16;
+    const int64_t NC = n_chunks(p);
+    if ((st = device_ready()) != KDA_OK) return st;
+    if (NC == 0) return copy_state(p, state_in, state_out, s);
+    const int64_t rc = range_of(p, range_chunks);
+    float* carry = state_out ? state_out : static_cast<float*>(workspace);
+    char* cards[2] = {static_cast<char*>(workspace) + state_bytes_of(p), nullptr};
+    cards[1] = cards[0] + range_card_bytes(p, rc);
+    auto range = [&](int64_t c0) {
+        const int64_t c1 = c0 + rc < NC ? c0 + rc : NC;
+        RangeLaunch r = range_launch(p, q, k, v, log_alpha, beta, g, out, cards[(c0 / rc) & 1], c0, c1);
+        r.sa.state_in = c0 == 0 ? state_in : carry;
+        r.sa.state_out = (c1 == NC && !state_out) ? nullptr : carry;
+        return r;
+    };
+    if (rc == NC) {   // one range: nothing to overlap
+        const RangeLaunch r = range(0);
+        if (launch_prepare(bf16, p->dk, r.pa, s) != hipSuccess) return KDA_ERR_HIP;
+        return hip_status(launch_scan(bf16, p->dk, false, r.sa, s));
+    }
+    // Events: the caller's prior work on `stream` (start), each card buffer
+    // filled (prepared[b]) and drained (scanned[b]), and the aux stream's end
+    // (joined), which `stream` waits on before returning, also on failure, so
+    // nothing of this call runs on aux after the caller's next work on `stream`.
+    enum { kStart, kPrep0, kPrep1, kScan0, kScan1, kJoin, kEvents };
+    hipEvent_t ev[kEvents] = {};
+    for (int i = 0; i < kEvents; ++i)
+        if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+            for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
+            return KDA_ERR_HIP;
+        }
+    bool ok = hipEventRecord(ev[kStart], s) == hipSuccess && hipStreamWaitEvent(aux, ev[kStart], 0) == hipSuccess;
+    for (int64_t c0 = 0, i = 0; ok && c0 < NC; c0 += rc, ++i) {
+        const int b = (int)(i & 1);
+        const RangeLaunch r = range(c0);
+        // range i's prepare on aux, once the scan of range i - 2 (same buffer) is done
+        ok = (i < 2 || hipStreamWaitEvent(aux, ev[kScan0 + b], 0) == hipSuccess) &&
+             launch_prepare(bf16, p->dk, r.pa, aux) == hipSuccess && hipEventRecord(ev[kPrep0 + b], aux) == hipSuccess &&
+             hipStreamWaitEvent(s, ev[kPrep0 + b], 0) == hipSuccess &&
+             launch_scan(bf16, p->dk, false, r.sa, s) == hipSuccess && hipEventRecord(ev[kScan0 + b], s) == hipSuccess;
+    }
+    const bool joined = hipEventRecord(ev[kJoin], aux) == hipSuccess && hipStreamWaitEvent(s, ev[kJoin], 0) == hipSuccess;
+    for (int i = 0; i < kEvents; ++i) hipEventDestroy(ev[i]);
+    return ok && joined ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_prefill_noalloc(const kda_problem* p, const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, const void* g, const float* state_in,
                                void* out, float* state_out, void* stream) {
@@ -340,10 +460,7 @@ kda_status kda_prefill_noalloc(const kda_problem* p, const void* q, const void* 
     hipStream_t s = (hipStream_t)stream;
     if (NC == 0) {   // no tokens: state_out = state_in (or 0); no cards
         if ((st = device_ready()) != KDA_OK) return st;
-        ScanArgs a = {};
-        a.state_in = state_in; a.state_out = state_out;
-        a.B = p->batch; a.T = 0; a.H = p->heads; a.NC = 0;
-        return hip_status(launch_scan(bf16, p->dk, false, a, s));
+        return copy_state(p, state_in, state_out, s);
     }
     const size_t BH = (size_t)p->batch * (size_t)p->heads;
     const size_t per_chunk = BH * card_bytes(bf16, p->dk);   // cards of one chunk index, all (row, head)
@@ -364,33 +481,13 @@ kda_status kda_prefill_noalloc(const kda_problem* p, const void* q, const void* 
     if ((st = scratch_address(&base)) != KDA_OK) return st;
     char* cards = static_cast<char*>(base) + cards_off;
     float* carry = state_out ? state_out : reinterpret_cast<float*>(base);
-    const size_t esz = bf16 ? 2 : 4;
-    const int64_t T = p->seqlen;
-    const int H = p->heads;
     for (int64_t c0 = 0; c0 < NC; c0 += per_pass) {
         const int64_t c1 = c0 + per_pass < NC ? c0 + per_pass : NC;
-        const int64_t t0 = c0 * 64, t1 = c1 * 64 < T ? c1 * 64 : T;
-        const size_t tok = (size_t)t0 * (size_t)H;   // row-0 offset of the range, in token-heads
-        PrepareArgs pa = {};
-        pa.q = static_cast<const char*>(q) + tok * p->dk * esz;
-        pa.k = static_cast<const char*>(k) + tok * p->dk * esz;
-        pa.v = static_cast<const char*>(v) + tok * p->dv * esz;
-        pa.log_alpha = log_alpha + tok * p->dk;
-        pa.beta = beta + tok;
-        pa.ws = cards;
-        pa.B = p->batch; pa.T = t1 - t0; pa.row_stride = T; pa.H = H; pa.NC = (int)(c1 - c0);
-        pa.floor_ = p->log_alpha_min;
-        hipError_t e = launch_prepare(bf16, p->dk, pa, s);
-        if (e != hipSuccess) return KDA_ERR_HIP;
-        ScanArgs sa = {};
-        sa.ws = cards;
-        sa.g = static_cast<const char*>(g) + tok * p->dv * esz;
-        sa.out = static_cast<char*>(out) + tok * p->dv * esz;
-        sa.state_in = c0 == 0 ? state_in : carry;
-        sa.state_out = (c1 == NC && !state_out) ? nullptr : carry;
-        sa.B = p->batch; sa.T = t1 - t0; sa.row_stride = T; sa.H = H; sa.NC = (int)(c1 - c0);
-        e = launch_scan(bf16, p->dk, false, sa, s);
-        if (e != hipSuccess) return KDA_ERR_HIP;
+        RangeLaunch r = range_launch(p, q, k, v, log_alpha, beta, g, out, cards, c0, c1);
+        r.sa.state_in = c0 == 0 ? state_in : carry;
+        r.sa.state_out = (c1 == NC && !state_out) ? nullptr : carry;
+        if (launch_prepare(bf16, p->dk, r.pa, s) != hipSuccess) return KDA_ERR_HIP;
+        if (launch_scan(bf16, p->dk, false, r.sa, s) != hipSuccess) return KDA_ERR_HIP;
     }
     return KDA_OK;
 }

@@ -208,6 +208,38 @@ kda_status kda_backward(const kda_problem* p, const void* q, const void* k, cons
                         float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of kda_prefill_pipelined with ranges of range_chunks
+ * chunks: the carried state (B*H*dk*dv fp32), then the update cards of one
+ * range for every (row, head), twice when the sequence spans more than one
+ * range, each part rounded up to 256 bytes.  Returns 0 if p is invalid or
+ * unsupported or range_chunks < 1. */
+size_t kda_pipelined_workspace_size(const kda_problem* p, int32_t range_chunks);
+
+/* Chunked prefill with the two stages overlapped [lotamate.com Kimi K3
+ * training analysis, §四 基础设施: FlashKDA overlaps the intra-chunk work with
+ * the state passed from chunk to chunk].  The sequence is cut into ranges of
+ * range_chunks whole chunks (the last may be shorter); the cards of range
+ * i + 1 are prepared on aux_stream into one of two buffers while the scan of
+ * range i runs on `stream` from the other, carrying the state from range to
+ * range, so the cards in use stay a bounded size.  Results are identical to
+ * kda_chunk_prepare + kda_chunk_scan on the same inputs.
+ *   q, k, v, log_alpha, beta, g, out, state_in, state_out: as for
+ *   kda_chunk_prepare and kda_chunk_scan (state_out may equal state_in).
+ *   range_chunks: >= 1 chunks per range.
+ *   workspace: >= kda_pipelined_workspace_size(p, range_chunks) bytes,
+ *   caller-owned; contents on entry unused.
+ *   stream, aux_stream: hipStream_t; aux_stream may equal stream (then the
+ *   ranges run one after the other).  aux_stream first waits for the work
+ *   already on `stream`, and `stream` waits for everything this call put on
+ *   aux_stream before any later work on `stream`, so the caller orders
+ *   against `stream` alone.  The call creates and releases its own HIP events.
+ * Errors as for the other calls; KDA_ERR_HIP also when an event cannot be
+ * created or recorded. */
+kda_status kda_prefill_pipelined(const kda_problem* p, const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta, const void* g,
+                                 const float* state_in, void* out, float* state_out, int32_t range_chunks,
+                                 void* workspace, size_t workspace_bytes, void* stream, void* aux_stream);
+
 /* Bytes of the fixed device scratch area of kda_prefill_noalloc (per GPU). */
 #define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

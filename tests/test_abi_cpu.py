@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -295,3 +295,40 @@ def test_prefill_noalloc_rejects_what_its_scratch_cannot_hold(L):
     if not _have_gpu():   # valid arguments get past validation to the (missing) device
         assert call(_p(batch=903, heads=1), so=FAKE) == 4
         assert call(_p()) == 4
+
+
+def test_pipelined_workspace_and_argument_errors(L):
+    """kda_prefill_pipelined: the workspace is the carried state plus one
+    range's cards, twice when the sequence spans several ranges; bad ranges,
+    pointers and workspaces are refused before any launch."""
+    card, state = 74240, 2 * 3 * 128 * 128 * 4            # _p(): B=2, H=3, T=200 -> 4 chunks
+    size = lambda pr, rc: L.kda_pipelined_workspace_size(ctypes.byref(pr), rc)
+    assert size(_p(), 1) == state + 2 * ((1 * 6 * card + 255) // 256 * 256)
+    assert size(_p(), 3) == state + 2 * 3 * 6 * card
+    assert size(_p(), 4) == state + 4 * 6 * card           # one range: one buffer
+    assert size(_p(), 2 ** 31 - 1) == state + 4 * 6 * card
+    assert size(_p(seqlen=0), 8) == state
+    assert size(_p(), 0) == 0 and size(_p(), -5) == 0
+    assert size(_p(dk=96, dv=96), 4) == 0
+    ws = size(_p(), 2)
+    call = lambda pr=_p(), rc=2, w=FAKE, n=ws, q=FAKE, so=None: L.kda_prefill_pipelined(
+        ctypes.byref(pr), q, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, so, rc, w, n, None, None)
+    assert call(rc=0) == 1
+    assert call(rc=-1) == 1
+    assert call(q=None) == 1
+    assert call(q=MISALIGNED) == 1
+    assert call(w=None) == 1
+    assert call(w=MISALIGNED) == 1
+    assert call(n=ws - 1) == 3
+    assert call(pr=_p(log_alpha_min=0.5)) == 1
+    assert call(pr=_p(dk=64, dv=128)) == 2
+    assert call(pr=_p(batch=0), w=None, n=0) == 0
+    if not _have_gpu():   # valid arguments get past validation to the (missing) device
+        assert call() == 4
+        assert call(pr=_p(seqlen=0), w=None, n=size(_p(seqlen=0), 2), so=FAKE) == 4
+
+
+def test_binding_checks_range_chunks():
+    for rc in (0, -1, 2 ** 31, 1.5):
+        with pytest.raises(ValueError, match="range_chunks"):
+            kda._range_chunks(rc)

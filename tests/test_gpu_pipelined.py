@@ -1,0 +1,132 @@
+"""kda_prefill_pipelined -- chunk ranges, the next range's cards prepared on a
+second stream while the current range is scanned -- against the fp64 oracle
+and against kda_chunk_prepare + kda_chunk_scan on the same inputs (needs an
+MI355X), through the C ABI.
+
+Each card depends only on its own chunk and the state crosses a range
+boundary in fp32, so the pipelined results must equal the two-call prefill
+bit for bit, whatever the range size, on either stream arrangement.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from kda_inputs import make_inputs, to_f64
+
+torch = pytest.importorskip("torch")
+import gated_delta_rule_91_amd as kda
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def note(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _inputs(B, T, H, d, io, seed, state0=True):
+    inp = make_inputs(B, T, H, d, d, io_dtype=io, seed=seed, alpha_min=0.9, logit_mu=-2.0, with_state0=state0)
+    return inp, kda.to_device(inp)
+
+
+def _reference(d, floor, state_in):
+    out, st = kda.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["g"], floor, state_in=state_in)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def _pipelined(d, floor, state_in, **kw):
+    out, st = kda.prefill_pipelined(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["g"], floor,
+                                    state_in=state_in, **kw)
+    torch.cuda.synchronize()
+    return out, st
+
+
+@pytest.mark.parametrize("B,T,H,d,io,rc", [
+    (2, 8192 - 37, 16, 128, "bf16", 7),    # 128 chunks in 19 ranges, ragged tail
+    (1, 4096, 32, 128, "bf16", 16),        # 4 ranges: both buffers reused
+    (1, 200, 4, 128, "bf16", 1),           # one chunk per range
+    (2, 1000, 3, 64, "bf16", 5),
+    (2, 4096, 8, 64, "f32", 5),
+    (1, 777, 2, 128, "f32", 3),
+    (3, 300, 2, 128, "bf16", 100),         # one range: no overlap
+])
+def test_pipelined_equals_prefill(B, T, H, d, io, rc):
+    inp, dd = _inputs(B, T, H, d, io, seed=900 + T % 97 + rc)
+    note(f"[pipelined] B={B} T={T} H={H} d={d} {io} range={rc}")
+    r_out, r_st = _reference(dd, inp.log_alpha_min, dd["state0"])
+    out, st = _pipelined(dd, inp.log_alpha_min, dd["state0"], range_chunks=rc)
+    assert torch.equal(out, r_out) and torch.equal(st, r_st)
+    # without state_out the state is carried through the workspace
+    out2, st2 = _pipelined(dd, inp.log_alpha_min, dd["state0"], range_chunks=rc, want_state=False)
+    assert st2 is None and torch.equal(out2, r_out)
+
+
+def test_pipelined_in_place_state_and_one_stream():
+    inp, dd = _inputs(2, 2000, 8, 128, "bf16", seed=931)
+    note("[pipelined] B=2 T=2000 H=8 d=128 bf16, state in place; aux stream = stream")
+    r_out, r_st = _reference(dd, inp.log_alpha_min, dd["state0"])
+    s = dd["state0"].clone()
+    out, st = _pipelined(dd, inp.log_alpha_min, s, state_out=s, range_chunks=4)
+    assert st.data_ptr() == s.data_ptr()
+    assert torch.equal(out, r_out) and torch.equal(st, r_st)
+    cur = torch.cuda.current_stream()
+    out, st = _pipelined(dd, inp.log_alpha_min, dd["state0"], range_chunks=3, aux_stream=cur)
+    assert torch.equal(out, r_out) and torch.equal(st, r_st)
+
+
+def test_pipelined_on_a_side_stream_with_reused_workspace():
+    """Work queued on a non-default stream: the aux stream waits for it, and
+    the results are ready once that stream is synchronised; a workspace
+    reused right away by a second call gives the same results."""
+    inp, dd = _inputs(1, 3000, 16, 128, "bf16", seed=932)
+    note("[pipelined] B=1 T=3000 H=16 d=128 bf16 on a side stream, reused workspace")
+    r_out, r_st = _reference(dd, inp.log_alpha_min, dd["state0"])
+    p = kda.problem(1, 3000, 16, 128, 128, kda.KDA_BF16, inp.log_alpha_min)
+    ws = torch.empty(kda.pipelined_workspace_size(p, 6), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q = dd["q"].clone()   # produced on the side stream just before the call
+        o1, s1 = kda.prefill_pipelined(q, dd["k"], dd["v"], dd["log_alpha"], dd["beta"], dd["g"],
+                                       inp.log_alpha_min, state_in=dd["state0"], range_chunks=6, workspace=ws)
+        o2, s2 = kda.prefill_pipelined(q, dd["k"], dd["v"], dd["log_alpha"], dd["beta"], dd["g"],
+                                       inp.log_alpha_min, state_in=dd["state0"], range_chunks=6, workspace=ws)
+    side.synchronize()
+    for o, s in ((o1, s1), (o2, s2)):
+        assert torch.equal(o, r_out) and torch.equal(s, r_st)
+
+
+def test_pipelined_empty_sequence():
+    note("[pipelined] T=0")
+    inp, dd = _inputs(2, 64, 3, 64, "f32", seed=933)
+    p_q = dd["q"][:, :0].contiguous()
+    k, v, la = dd["k"][:, :0].contiguous(), dd["v"][:, :0].contiguous(), dd["log_alpha"][:, :0].contiguous()
+    beta, g = dd["beta"][:, :0].contiguous(), dd["g"][:, :0].contiguous()
+    out, st = kda.prefill_pipelined(p_q, k, v, la, beta, g, inp.log_alpha_min, state_in=dd["state0"],
+                                    range_chunks=2)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and torch.equal(st, dd["state0"])
+    out, st = kda.prefill_pipelined(p_q, k, v, la, beta, g, inp.log_alpha_min, range_chunks=2)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st).item() == 0
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_pipelined_vs_oracle(io):
+    B, T, H, d = 2, 1000, 2, 128
+    inp, dd = _inputs(B, T, H, d, io, seed=934)
+    note(f"[pipelined] vs oracle B={B} T={T} H={H} d={d} {io} range=3")
+    out, st = _pipelined(dd, inp.log_alpha_min, dd["state0"], range_chunks=3)
+    f = lambda a: to_f64(a, inp.io_dtype)
+    r_out, r_st = oracle.kda_ref(f(inp.q), f(inp.k), f(inp.v), inp.log_alpha, inp.beta, f(inp.g),
+                                 inp.log_alpha_min, inp.state0)
+    go = out.float().cpu().numpy().astype(np.float64)
+    gs = st.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            eo = np.linalg.norm(go[b, :, h] - r_out[b, :, h]) / np.linalg.norm(r_out[b, :, h])
+            es = np.linalg.norm(gs[b, h] - r_st[b, h]) / np.linalg.norm(r_st[b, h])
+            assert eo <= TOL[io] and es <= TOL[io], (b, h, eo, es)
