@@ -35,6 +35,9 @@ Also reported on the same JSON line:
   * the backward pass (gradients of every prefill input and of the initial
     state) on the medium prefill workload B=4, T=4,096, H=16, d=128 bf16:
     ms per call and token-heads/s, beside the forward on the same inputs;
+    and the split pair for training, a prefill that keeps its cards and
+    chunk states (kda_prefill_for_backward) and the backward without its
+    forward pass (kda_backward_after_prefill);
   * cpu_baseline: the fp64 oracle (its source compiled -march=native for the
     host) timed over the whole long workload on the CPU share given to the
     job, with the host's CPU count and model.
@@ -483,11 +486,41 @@ def main():
         # gradient-kernel products per token-head: five C x d x d (with a state), nine C x C x d
         bwd_flop = 5 * 2 * D * D + 9 * 2 * C * D
         log(f"[bench] backward {bms:.3f} ms, forward {fms:.3f} ms on {Wb['name']}")
+        # the split pair: a prefill that keeps its cards and chunk states in
+        # the backward workspace, then the backward without its forward pass
+        fwd_out = torch.empty_like(db["g"])
+
+        def fkeep():
+            kda.prefill_for_backward(db["q"], db["k"], db["v"], db["log_alpha"], db["beta"], db["g"], floor_b,
+                                     out=fwd_out, workspace=wsb)
+
+        def bafter():
+            return kda.backward_after_prefill(db["q"], db["k"], db["v"], db["log_alpha"], db["beta"], db["g"],
+                                              fwd_out, wsb, floor_b, d_out=d_out, d_state=d_state)
+
+        ref = bstep()
+        fkeep()
+        got = bafter()
+        torch.cuda.synchronize()
+        same = all(torch.equal(got[n], ref[n]) for n in ref)
+        e0.record()
+        for _ in range(reps):
+            fkeep()
+        e1.record()
+        for _ in range(reps):
+            bafter()
+        e2.record()
+        torch.cuda.synchronize()
+        kms, ams = e0.elapsed_time(e1) / reps, e1.elapsed_time(e2) / reps
+        log(f"[bench] prefill keeping the forward {kms:.3f} ms, backward after it {ams:.3f} ms "
+            f"(identical to the backward: {same})")
         result["backward"] = {"workload": Wb["name"], "ms": bms, "forward_ms": fms, "ratio_to_forward": bms / fms,
                               "token_heads_per_s": th / (bms * 1e-3), "GBps": bwd_bytes * th / (bms * 1e-3) / 1e9,
                               "bytes_per_token_head": bwd_bytes, "grad_flop_per_token_head": bwd_flop,
-                              "grad_TFLOPs_over_whole_call": bwd_flop * th / (bms * 1e-3) / 1e12}
-        del db, wsb, d_out, d_state
+                              "grad_TFLOPs_over_whole_call": bwd_flop * th / (bms * 1e-3) / 1e12,
+                              "after_prefill": {"prefill_for_backward_ms": kms, "ms": ams,
+                                                "ratio_to_forward": ams / fms, "identical_to_backward": same}}
+        del db, wsb, d_out, d_state, fwd_out, ref, got
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- cpu baseline

@@ -9,7 +9,8 @@ CPU or PyTorch fallback: if the library is missing, every call raises.
 Entry points (same names as the C ABI, minus the ``kda_`` prefix):
     workspace_size, chunk_prepare, chunk_scan, chunk_scan_checkpoints, segment_summarize,
     segment_combine, decode_step, backward_workspace_size, backward,
-    varlen_workspace_size, varlen_prepare, varlen_scan, pipelined_workspace_size
+    varlen_workspace_size, varlen_prepare, varlen_scan, prefill_for_backward,
+    backward_after_prefill, pipelined_workspace_size
 Conveniences built from them: prefill, segmented_prefill, varlen_prefill.
 prefill_pipelined calls kda_prefill_pipelined (chunk ranges, the next range's
 cards prepared on a second stream during the current range's scan);
@@ -33,7 +34,8 @@ EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_chu
            "kda_segment_summarize",
            "kda_segment_combine", "kda_decode_step", "kda_backward_workspace_size", "kda_backward",
            "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan",
-           "kda_pipelined_workspace_size", "kda_prefill_pipelined", "kda_prefill_noalloc", "kda_status_string")
+           "kda_prefill_for_backward", "kda_backward_after_prefill", "kda_pipelined_workspace_size",
+           "kda_prefill_pipelined", "kda_prefill_noalloc", "kda_status_string")
 # bytes of kda_prefill_noalloc's fixed per-GPU scratch area (KDA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.kda_varlen_workspace_size.restype = SZ
         L.kda_varlen_prepare.argtypes = [PP, I64, P, P, P, P, P, P, P, SZ, P]
         L.kda_varlen_scan.argtypes = [PP, I64, P, P, SZ, P, P, P, P, P]
+        L.kda_prefill_for_backward.argtypes = [PP] + [P] * 10 + [SZ, P]
+        L.kda_backward_after_prefill.argtypes = [PP] + [P] * 17 + [SZ, P]
         L.kda_pipelined_workspace_size.argtypes = [PP, I32]
         L.kda_pipelined_workspace_size.restype = SZ
         L.kda_prefill_pipelined.argtypes = [PP, P, P, P, P, P, P, P, P, P, I32, P, SZ, P, P]
@@ -329,6 +333,59 @@ def backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, d
         else None
     _check("kda_backward", lib().kda_backward(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g), _ptr(state_in),
+        _ptr(d_out), _ptr(d_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dlog_alpha"]),
+        _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace), workspace.numel(),
+        _stream(stream, q.device)))
+    return r
+
+
+def prefill_for_backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, out=None,
+                         state_out=None, want_state: bool = True, workspace=None, stream=None):
+    """Prefill that leaves its cards and chunk states in a backward workspace
+    (kda_prefill_for_backward).  Returns (out, state_out, workspace); pass
+    out and workspace to backward_after_prefill with the same inputs."""
+    torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_in", state_in, (B, H, dk, dv), torch.float32, q.device)
+    _expect("out", out, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_out", state_out, (B, H, dk, dv), torch.float32, q.device)
+    p = _problem_of(q, v, log_alpha_min)
+    nbytes = backward_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device)
+    if out is None:
+        out = torch.empty_like(g)
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check("kda_prefill_for_backward", lib().kda_prefill_for_backward(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g), _ptr(state_in),
+        _ptr(out), _ptr(state_out), _ptr(workspace), workspace.numel(), _stream(stream, q.device)))
+    return out, state_out, workspace
+
+
+def backward_after_prefill(q, k, v, log_alpha, beta, g, out, workspace, log_alpha_min: float, d_out=None,
+                           d_state=None, want_dstate: bool = True, stream=None) -> dict:
+    """backward() without its forward pass: out and workspace come from
+    prefill_for_backward on the same inputs.  Returns the same dict."""
+    torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
+    p = _problem_of(q, v, log_alpha_min)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("out", out, (B, T, H, dv), q.dtype, q.device)
+    _expect("d_out", d_out, (B, T, H, dv), q.dtype, q.device)
+    _expect("d_state", d_state, (B, H, dk, dv), torch.float32, q.device)
+    _expect_workspace(workspace, q.device)
+    r = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+             dlog_alpha=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta))
+    r["dstate0"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_dstate else None
+    _check("kda_backward_after_prefill", lib().kda_backward_after_prefill(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g), _ptr(out),
         _ptr(d_out), _ptr(d_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dlog_alpha"]),
         _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace), workspace.numel(),
         _stream(stream, q.device)))

@@ -350,30 +350,84 @@ size_t kda_backward_workspace_size(const kda_problem* p) {
     return backward_workspace_bytes(p->io_dtype == KDA_BF16, p->batch, p->seqlen, p->heads, p->dk);
 }
 
-kda_status kda_backward(const kda_problem* p, const void* q, const void* k, const void* v, const float* log_alpha,
-                        const float* beta, const void* g, const float* state_in, const void* d_out,
-                        const float* d_state, void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
-                        void* dg, float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks and the launch arguments shared by kda_backward and
+// kda_backward_after_prefill.
+static kda_status backward_args(const kda_problem* p, const void* q, const void* k, const void* v,
+                                const float* log_alpha, const float* beta, const void* g, const float* state_in,
+                                const void* out, bool need_out, const void* d_out, const float* d_state, void* dq,
+                                void* dk, void* dv, float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
+                                void* workspace, size_t workspace_bytes, BackwardArgs* a, bool* work) {
     kda_status st = check_problem(p);
     if (st != KDA_OK) return st;
     const bool tokens = p->batch > 0 && p->seqlen > 0;
     if (!ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) || !ok_ptr(log_alpha, tokens) ||
         !ok_beta(beta, tokens) || !ok_ptr(g, tokens) || !ok_ptr(dq, tokens) || !ok_ptr(dk, tokens) ||
         !ok_ptr(dv, tokens) || !ok_ptr(dlog_alpha, tokens) || !ok_beta(dbeta, tokens) || !ok_ptr(dg, tokens) ||
-        !ok_ptr(workspace, tokens) || !ok_opt_ptr(state_in) || !ok_opt_ptr(d_out) || !ok_opt_ptr(d_state) ||
-        !ok_opt_ptr(d_state_in))
+        !ok_ptr(workspace, tokens) || !ok_ptr(out, need_out && tokens) || !ok_opt_ptr(state_in) ||
+        !ok_opt_ptr(d_out) || !ok_opt_ptr(d_state) || !ok_opt_ptr(d_state_in))
         return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < kda_backward_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
-    if (p->batch == 0 || (!tokens && !d_state_in)) return KDA_OK;
+    *work = !(p->batch == 0 || (!tokens && !d_state_in));
+    if (!*work) return KDA_OK;
     if ((st = device_ready()) != KDA_OK) return st;
-    BackwardArgs a;
+    a->q = q; a->k = k; a->v = v; a->log_alpha = log_alpha; a->beta = beta; a->g = g; a->state_in = state_in;
+    a->d_out = d_out; a->d_state = d_state;
+    a->dq = dq; a->dk = dk; a->dv = dv; a->dlog_alpha = dlog_alpha; a->dbeta = dbeta; a->dg = dg;
+    a->d_state_in = d_state_in;
+    a->out = out;
+    a->ws = static_cast<char*>(workspace);
+    a->B = p->batch; a->T = p->seqlen; a->H = p->heads; a->NC = (int)n_chunks(p); a->floor_ = p->log_alpha_min;
+    return KDA_OK;
+}
+
+kda_status kda_backward(const kda_problem* p, const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const void* g, const float* state_in, const void* d_out,
+                        const float* d_state, void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta,
+                        void* dg, float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+    BackwardArgs a = {};
+    bool work = false;
+    const kda_status st = backward_args(p, q, k, v, log_alpha, beta, g, state_in, nullptr, false, d_out, d_state,
+                                        dq, dk, dv, dlog_alpha, dbeta, dg, d_state_in, workspace, workspace_bytes,
+                                        &a, &work);
+    if (st != KDA_OK || !work) return st;
+    return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, true, (hipStream_t)stream));
+}
+
+kda_status kda_prefill_for_backward(const kda_problem* p, const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const float* beta, const void* g,
+                                    const float* state_in, void* out, float* state_out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    kda_status st = check_problem(p);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->batch > 0 && p->seqlen > 0;
+    if (!ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) || !ok_ptr(log_alpha, tokens) ||
+        !ok_beta(beta, tokens) || !ok_ptr(g, tokens) || !ok_ptr(out, tokens) || !ok_ptr(workspace, tokens) ||
+        !ok_opt_ptr(state_in) || !ok_opt_ptr(state_out))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_backward_workspace_size(p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (p->batch == 0 || (!tokens && !state_out)) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!tokens) return copy_state(p, state_in, state_out, s);
+    BackwardArgs a = {};
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.g = g; a.state_in = state_in;
-    a.d_out = d_out; a.d_state = d_state;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dg = dg;
-    a.d_state_in = d_state_in;
     a.ws = static_cast<char*>(workspace);
     a.B = p->batch; a.T = p->seqlen; a.H = p->heads; a.NC = (int)n_chunks(p); a.floor_ = p->log_alpha_min;
-    return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, (hipStream_t)stream));
+    return hip_status(launch_backward_forward(p->io_dtype == KDA_BF16, p->dk, a, out, state_out, s));
+}
+
+kda_status kda_backward_after_prefill(const kda_problem* p, const void* q, const void* k, const void* v,
+                                      const float* log_alpha, const float* beta, const void* g, const void* out,
+                                      const void* d_out, const float* d_state, void* dq, void* dk, void* dv,
+                                      float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    BackwardArgs a = {};
+    bool work = false;
+    const kda_status st = backward_args(p, q, k, v, log_alpha, beta, g, nullptr, out, true, d_out, d_state, dq,
+                                        dk, dv, dlog_alpha, dbeta, dg, d_state_in, workspace, workspace_bytes, &a,
+                                        &work);
+    if (st != KDA_OK || !work) return st;
+    return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, false, (hipStream_t)stream));
 }
 
 size_t kda_pipelined_workspace_size(const kda_problem* p, int32_t range_chunks) {

@@ -624,7 +624,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     // ---- 4: value columns in blocks of NB ----
     const E* vp = reinterpret_cast<const E*>(a.v);
     const E* gp = reinterpret_cast<const E*>(a.g);
-    const E* op = reinterpret_cast<const E*>(a.ws + L.out);
+    const E* op = reinterpret_cast<const E*>(a.out);
     const E* dop = reinterpret_cast<const E*>(a.d_out);
     E* dvp = reinterpret_cast<E*>(a.dv);
     E* dgp = reinterpret_cast<E*>(a.dg);
@@ -1048,26 +1048,35 @@ size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk) 
     return T == 0 ? 0 : BwdLayout(bf16, B, T, H, dk).total;
 }
 
-hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t s) {
+hipError_t launch_backward_forward(bool bf16, int dk, const BackwardArgs& a, void* out, float* state_out,
+                                   hipStream_t s) {
+    if (a.NC == 0 || a.B == 0) return hipSuccess;
     const BwdLayout L(bf16, a.B, a.T, a.H, dk);
-    if (a.NC > 0 && a.B > 0) {   // forward cards, then the forward hand-off keeping every chunk's entering state
-        PrepareArgs p = {};
-        p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.beta = a.beta;
-        p.ws = a.ws + L.cards;
-        p.B = a.B; p.T = a.T; p.H = a.H; p.NC = a.NC; p.floor_ = a.floor_;
-        hipError_t e = launch_prepare(bf16, dk, p, s);
-        if (e != hipSuccess) return e;
-        ScanArgs f = {};
-        f.ws = a.ws + L.cards;
-        f.g = a.g; f.state_in = a.state_in; f.out = a.ws + L.out;
-        f.states = reinterpret_cast<float*>(a.ws + L.states);
-        f.ckpt_every = 1;
-        f.B = a.B; f.T = a.T; f.H = a.H; f.NC = a.NC;
-        e = launch_scan(bf16, dk, false, f, s);
+    PrepareArgs p = {};
+    p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.beta = a.beta;
+    p.ws = a.ws + L.cards;
+    p.B = a.B; p.T = a.T; p.H = a.H; p.NC = a.NC; p.floor_ = a.floor_;
+    hipError_t e = launch_prepare(bf16, dk, p, s);
+    if (e != hipSuccess) return e;
+    ScanArgs f = {};
+    f.ws = a.ws + L.cards;
+    f.g = a.g; f.state_in = a.state_in; f.out = out; f.state_out = state_out;
+    f.states = reinterpret_cast<float*>(a.ws + L.states);
+    f.ckpt_every = 1;
+    f.B = a.B; f.T = a.T; f.H = a.H; f.NC = a.NC;
+    return launch_scan(bf16, dk, false, f, s);
+}
+
+hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, bool recompute, hipStream_t s) {
+    BackwardArgs b = a;
+    if (recompute) {   // forward cards, then the forward hand-off keeping every chunk's entering state
+        const BwdLayout L(bf16, a.B, a.T, a.H, dk);
+        b.out = a.ws + L.out;
+        const hipError_t e = launch_backward_forward(bf16, dk, b, a.ws + L.out, nullptr, s);
         if (e != hipSuccess) return e;
     }
-    if (bf16) return dk == 128 ? launch_backward_t<__bf16, 128>(a, s) : launch_backward_t<__bf16, 64>(a, s);
-    return dk == 128 ? launch_backward_t<float, 128>(a, s) : launch_backward_t<float, 64>(a, s);
+    if (bf16) return dk == 128 ? launch_backward_t<__bf16, 128>(b, s) : launch_backward_t<__bf16, 64>(b, s);
+    return dk == 128 ? launch_backward_t<float, 128>(b, s) : launch_backward_t<float, 64>(b, s);
 }
 
 }  // namespace kda

@@ -84,6 +84,8 @@ struct BackwardArgs {
     float* dbeta;            // [B,T,H]
     void* dg;                // [B,T,H,dv] io dtype
     float* d_state_in;       // [B,H,dk,dv] or null
+    const void* out;         // the forward output [B,T,H,dv] io dtype (set by launch_backward when it
+                             // recomputes the forward)
     char* ws;                // backward_workspace_bytes
     int64_t B, T;
     int H, NC;
@@ -92,7 +94,14 @@ struct BackwardArgs {
 
 size_t card_bytes(bool bf16, int dk);
 size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk);
-hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, hipStream_t s);
+// The forward part of the backward: cards and every chunk's entering state
+// into the backward workspace, the output to `out`, the final state to
+// state_out (or nowhere).
+hipError_t launch_backward_forward(bool bf16, int dk, const BackwardArgs& a, void* out, float* state_out,
+                                   hipStream_t s);
+// The backward; recompute: run the forward part first (its output into the
+// workspace), else the workspace already holds it and a.out is the output.
+hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, bool recompute, hipStream_t s);
 hipError_t launch_prepare(bool bf16, int dk, const PrepareArgs& a, hipStream_t s);
 hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s);
 // segment summaries of bf16 cards at d_k = d_v = 128 with whole 16-column

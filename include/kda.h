@@ -182,8 +182,10 @@ kda_status kda_varlen_scan(const kda_problem* p, int64_t n_seq, const int32_t* c
                            const void* workspace, size_t workspace_bytes, const void* g,
                            const float* state_in, void* out, float* state_out, void* stream);
 
-/* Bytes of scratch kda_backward needs for problem p: the state entering every
- * chunk plus the 64 states entering one chunk's tokens, fp32, per (b, h).
+/* Bytes of scratch kda_backward needs for problem p: per (b, h), the update
+ * card and the reverse-pass card of every chunk, the forward output, the
+ * state entering every chunk plus the final state, and the state gradient
+ * leaving every chunk (fp32 states), each region rounded up to 256 bytes.
  * Returns 0 if p is invalid or unsupported, or if p has no tokens. */
 size_t kda_backward_workspace_size(const kda_problem* p);
 
@@ -207,6 +209,34 @@ kda_status kda_backward(const kda_problem* p, const void* q, const void* k, cons
                         const void* d_out, const float* d_state, void* dq, void* dk, void* dv,
                         float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Prefill for training: the output and final state of kda_chunk_prepare +
+ * kda_chunk_scan, computed so that the update cards and the state entering
+ * every chunk stay in a kda_backward workspace for kda_backward_after_prefill
+ * [zuoshipin.com/article/18261 §四: the kernels serve training throughput;
+ * the forward's hand-off states are what the backward consumes].
+ *   q, k, v, log_alpha, beta, g, state_in, out, state_out: as for
+ *   kda_chunk_prepare and kda_chunk_scan (state_out may equal state_in).
+ *   workspace: >= kda_backward_workspace_size(p) bytes, caller-owned; it then
+ *   holds the forward pass of these inputs until it is reused. */
+kda_status kda_prefill_for_backward(const kda_problem* p, const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const float* beta, const void* g,
+                                    const float* state_in, void* out, float* state_out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* kda_backward without its forward pass: the same gradients, read from the
+ * workspace that kda_prefill_for_backward filled for the same problem and the
+ * same q, k, v, log_alpha, beta, g and state_in, with `out` the output it
+ * wrote (unchanged since).  Other arguments as for kda_backward (there is no
+ * state_in: the workspace holds the state entering every chunk).  Inputs that
+ * differ from that prefill's give gradients of the wrong point; this is not
+ * checked.  The workspace keeps the forward pass, so a second call with other
+ * d_out / d_state is valid too. */
+kda_status kda_backward_after_prefill(const kda_problem* p, const void* q, const void* k, const void* v,
+                                      const float* log_alpha, const float* beta, const void* g, const void* out,
+                                      const void* d_out, const float* d_state, void* dq, void* dk, void* dv,
+                                      float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of kda_prefill_pipelined with ranges of range_chunks
  * chunks: the carried state (B*H*dk*dv fp32), then the update cards of one

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -332,3 +332,35 @@ def test_binding_checks_range_chunks():
     for rc in (0, -1, 2 ** 31, 1.5):
         with pytest.raises(ValueError, match="range_chunks"):
             kda._range_chunks(rc)
+
+
+def test_prefill_for_backward_and_backward_after_prefill_argument_errors(L):
+    """The split training pair takes a kda_backward workspace; the backward
+    half also needs the forward output.  Bad arguments are refused before
+    any launch."""
+    p = _p()
+    ws = L.kda_backward_workspace_size(ctypes.byref(p))
+    fwd = lambda pr=p, q=FAKE, o=FAKE, w=FAKE, n=ws, si=None, so=None: L.kda_prefill_for_backward(
+        ctypes.byref(pr), q, FAKE, FAKE, FAKE, FAKE, FAKE, si, o, so, w, n, None)
+    assert fwd(q=None) == 1
+    assert fwd(o=None) == 1
+    assert fwd(o=MISALIGNED) == 1
+    assert fwd(w=None) == 1
+    assert fwd(si=MISALIGNED) == 1
+    assert fwd(n=ws - 1) == 3
+    assert fwd(pr=_p(dk=64, dv=128)) == 2
+    assert fwd(pr=_p(batch=0), q=None, o=None, w=None, n=0) == 0
+    assert fwd(pr=_p(seqlen=0), q=None, o=None, w=None, n=0) == 0        # no state_out: nothing to do
+    bwd = lambda pr=p, o=FAKE, w=FAKE, n=ws, dq=FAKE, dsi=None: L.kda_backward_after_prefill(
+        ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, o, None, None, dq, FAKE, FAKE, FAKE, FAKE, FAKE,
+        dsi, w, n, None)
+    assert bwd(o=None) == 1
+    assert bwd(o=MISALIGNED) == 1
+    assert bwd(dq=None) == 1
+    assert bwd(w=None) == 1
+    assert bwd(n=ws - 1) == 3
+    assert bwd(pr=_p(log_alpha_min=0.5)) == 1
+    assert bwd(pr=_p(seqlen=0), o=None, w=None, n=0, dq=None) == 0      # no d_state_in: nothing to do
+    if not _have_gpu():   # valid arguments get past validation to the (missing) device
+        assert fwd() == 4
+        assert bwd() == 4

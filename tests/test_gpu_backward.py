@@ -182,3 +182,31 @@ def test_backward_floored_channels_and_long_sequence():
     dla = gr["dlog_alpha"].cpu().numpy()
     assert np.all(dla[floored] == 0.0)
     assert np.count_nonzero(dla[~floored]) > 0.9 * (~floored).sum()
+
+
+@pytest.mark.parametrize("B,T,H,d,io", [(2, 300, 3, 128, "bf16"), (1, 777, 2, 64, "f32"), (3, 64, 2, 128, "f32"),
+                                        (1, 4096, 16, 128, "bf16")])
+def test_backward_after_prefill_equals_backward(B, T, H, d, io):
+    """kda_prefill_for_backward + kda_backward_after_prefill give what
+    kda_chunk_prepare + kda_chunk_scan and kda_backward give, bit for bit:
+    the same kernels run, the backward half just reuses the forward's cards,
+    chunk states and output.  A second backward call on the same workspace
+    with another d_out reuses them again."""
+    inp = make_inputs(B, T, H, d, d, io_dtype=io, seed=7700 + T, alpha_min=0.9, logit_mu=-1.0, with_state0=True)
+    t = kda.to_device(inp)
+    note(f"[backward after prefill] B={B} T={T} H={H} d={d} {io}")
+    args = (t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["g"])
+    gen = torch.Generator(device=DEV).manual_seed(T)
+    dout = torch.randn(t["g"].shape, device=DEV, generator=gen).to(t["g"].dtype)
+    dout2 = torch.randn(t["g"].shape, device=DEV, generator=gen).to(t["g"].dtype)
+    dst = torch.randn((B, H, d, d), device=DEV, generator=gen)
+    r_out, r_st = kda.prefill(*args, inp.log_alpha_min, state_in=t["state0"])
+    out, st, ws = kda.prefill_for_backward(*args, inp.log_alpha_min, state_in=t["state0"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, r_out) and torch.equal(st, r_st)
+    for do, ds in ((dout, dst), (dout2, None)):
+        ref = kda.backward(*args, inp.log_alpha_min, state_in=t["state0"], d_out=do, d_state=ds)
+        got = kda.backward_after_prefill(*args, out, ws, inp.log_alpha_min, d_out=do, d_state=ds)
+        torch.cuda.synchronize()
+        for name in ref:
+            assert torch.equal(got[name], ref[name]), name
