@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
     __syncthreads();
 
     const char* bcards = a.ws + L.bcards + (size_t)bh * NC * BC::BYTES;
-    float* dstates = reinterpret_cast<float*>(a.ws + L.dstates) + (size_t)bh * NC * DK * DV + col0 + n;
+    float* dstates = reinterpret_cast<float*>(a.ws + L.dstates) + (size_t)bh * NC * DK * DV;
     // one chunk's operands in registers: a two-slot ring loads chunk c - 1
     // while chunk c computes (loads are unconditional: past chunk 0 the ring
     // re-reads chunk 0)
@@ -302,11 +302,10 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
         }
     };
     auto step = [&](const Ops& o, int c) {
-        float* dst = dstates + (size_t)c * DK * DV;   // gradient of the state leaving chunk c
+        float* dst = dstates + (size_t)c * DK * DV;   // gradient of the state leaving chunk c, tiled
 #pragma unroll
         for (int mt = 0; mt < MTS; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[(size_t)((DK / 4) * w + 16 * mt + 4 * g + e) * DV] = dS[mt][e];
+            *reinterpret_cast<f32x4*>(dst + tiled_state_index(DK, tile, (DK / 16) * w + 4 * mt + g, n)) = dS[mt];
         // dU rows 16w..16w+15 = P^T dO + Ke dS
         f32x4 du = o.dul;
 #pragma unroll
@@ -635,10 +634,14 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 #pragma unroll
     for (int j = 0; j < 4; ++j) dMP[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 dbp = {0.f, 0.f, 0.f, 0.f};
+    // The states are stored tiled (tiled_state_index): a block of NB = 16
+    // columns is one contiguous tile, and piece idx of it holds rows
+    // 4 (idx / 16) .. + 3 of column idx % 16.
+    static_assert(NB == 16 && NTH % 16 == 0, "one tile per column block; a row group's 16 pieces in 16 adjacent lanes");
     constexpr int NSI = (DK * NB / 4 + NTH - 1) / NTH;   // staged 4-float pieces per thread
-    float rowp[NSI];   // rowsum(S0 * dS) over the blocks so far, row (idx / 4) of piece idx
+    f32x4 rowp[NSI];   // rowsum(S0 * dS) over the blocks so far: rows 4 (idx / 16) + e, column idx % 16
 #pragma unroll
-    for (int j = 0; j < NSI; ++j) rowp[j] = 0.f;
+    for (int j = 0; j < NSI; ++j) rowp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the global inputs of a column block, fetched one block ahead into
     // registers (every load unconditional: addresses are clamped, the block
     // after the last re-reads the last)
@@ -648,13 +651,14 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     };
     auto fetch = [&](int vb) {
         Pre p;
-        const int col0 = NB * (vb < DV / NB ? vb : DV / NB - 1);
+        const int tb = vb < DV / NB ? vb : DV / NB - 1;
+        const int col0 = NB * tb;
 #pragma unroll
         for (int j = 0; j < NSI; ++j) {
             const int idx = t + j * NTH < DK * NB / 4 ? t + j * NTH : DK * NB / 4 - 1;
-            const int row = idx / (NB / 4), c4 = (idx % (NB / 4)) * 4;
-            p.s[j] = *reinterpret_cast<const f32x4*>(S0 + (size_t)row * DV + col0 + c4);
-            p.d[j] = *reinterpret_cast<const f32x4*>(dSo + (size_t)row * DV + col0 + c4);
+            const int o = tiled_state_index(DK, tb, idx / 16, idx % 16);
+            p.s[j] = *reinterpret_cast<const f32x4*>(S0 + o);
+            p.d[j] = *reinterpret_cast<const f32x4*>(dSo + o);
         }
         // both halves load three values per element (the V pointer twice on
         // half 0), so no load sits under a branch
@@ -695,11 +699,14 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         for (int j = 0; j < NSI; ++j) {
             const int idx = t + j * NTH;
             if (idx < DK * NB / 4) {
-                const int row = idx / (NB / 4), c4 = (idx % (NB / 4)) * 4;
+                const int r0 = 4 * (idx / 16), c = idx % 16;
                 const f32x4 x = pre.s[j], y = pre.d[j];
-                st4(sS0 + row * LDSB + c4, x);
-                st4(sDS + row * LDSB + c4, y);
-                rowp[j] += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sS0[(r0 + e) * LDSB + c] = x[e];
+                    sDS[(r0 + e) * LDSB + c] = y[e];
+                }
+                rowp[j] += x * y;
             }
         }
         const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
@@ -855,14 +862,16 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         __syncthreads();
     }
 
-    // rowsum(S0 * dS): the four pieces of a row sit in adjacent lanes; q^ back over the state blocks
+    // rowsum(S0 * dS): the 16 columns of a row group sit in 16 adjacent lanes; q^ back over the state blocks
 #pragma unroll
     for (int j = 0; j < NSI; ++j) {
-        float x = rowp[j];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
+        f32x4 x = rowp[j];
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] += __shfl_xor(x[e], m);
         const int idx = t + j * NTH;
-        if (idx < DK * NB / 4 && (idx & 3) == 0) sDGC[4 * DK + idx / (NB / 4)] = x;
+        if (idx < DK * NB / 4 && (idx & 15) == 0) st4(sDGC + 4 * DK + 4 * (idx / 16), x);
     }
     load_qhat();
 
@@ -1063,6 +1072,7 @@ hipError_t launch_backward_forward(bool bf16, int dk, const BackwardArgs& a, voi
     f.g = a.g; f.state_in = a.state_in; f.out = out; f.state_out = state_out;
     f.states = reinterpret_cast<float*>(a.ws + L.states);
     f.ckpt_every = 1;
+    f.states_tiled = true;
     f.B = a.B; f.T = a.T; f.H = a.H; f.NC = a.NC;
     return launch_scan(bf16, dk, false, f, s);
 }

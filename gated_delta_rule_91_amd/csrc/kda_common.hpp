@@ -36,6 +36,18 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
+// The backward's per-chunk fp32 states (the state entering every chunk and
+// the state gradient leaving it) are stored in 16-column tiles, and inside a
+// tile four consecutive rows of one column are contiguous: element (row, col)
+// of a d_k x d_v state sits at tiled_state_index(d_k, col / 16, row / 4,
+// col % 16) + row % 4.  A lane that holds rows 4i..4i+3 of one column (the
+// accumulator layout of the hand-off kernels) writes them with one 16-byte
+// store, a wave's 64 lanes one contiguous kilobyte, and one 16-column block
+// of the state is a contiguous d_k x 16 region.
+__host__ __device__ constexpr int tiled_state_index(int dk, int tile, int row4, int n) {
+    return ((tile * (dk / 4) + row4) * 16 + n) * 4;
+}
+
 // ---- MFMA policy ------------------------------------------------------------
 template <typename E> struct MM;
 

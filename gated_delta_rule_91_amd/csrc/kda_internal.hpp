@@ -36,6 +36,8 @@ struct ScanArgs {
     float* states;           // or null; else checkpoints [B,H,ceil(NC/ckpt_every)+1,dk,dv]: slot j is the
                              // state entering chunk j*ckpt_every, the last slot the final state
     int ckpt_every;          // chunks between checkpoints (>= 1 when states is set)
+    bool states_tiled;       // with states and ckpt_every 1: the backward's layout (tiled_state_index),
+                             // slot NC (the final state) not written
     int64_t B, T;            // packed variable-length batches: B = sequences, T = packed tokens
     int64_t row_stride;      // uniform batch: tokens between batch rows of g and out (0 = T)
     int H, NC;

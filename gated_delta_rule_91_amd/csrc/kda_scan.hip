@@ -157,7 +157,9 @@ constexpr int kPrefetchMulti = 1;
 
 // CKPT: 0 no checkpoints; 1 the state entering every chunk (unconditional
 // stores); 2 every ckpt_every chunks (a branch around the stores: the cheaper
-// choice when checkpoints are sparse)
+// choice when checkpoints are sparse); 3 the state entering every chunk in
+// the backward's tiled layout (one 16-byte store per lane and 16-row tile),
+// no final-state slot
 template <typename E, int DK, int NTW, bool SUMMARY, int CKPT>
 __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     using M = MM<E>;
@@ -260,7 +262,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     auto step = [&](auto full, const O& cur, int c) {
         constexpr bool FULL = decltype(full)::value;
         asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
-        if constexpr (CKPT != 0) {   // the state entering chunk c, to slot c / every
+        if constexpr (CKPT == 3) {   // the state entering chunk c, tiled
+            float* dst = a.states + ((size_t)bh * (NC + 1) + c) * DK * DK;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MTS; ++mt)
+                    *reinterpret_cast<f32x4*>(dst + tiled_state_index(DK, tile0 + j, (DK / 16) * w + 4 * mt + g, n)) =
+                        S[j][mt];
+        } else if constexpr (CKPT != 0) {   // the state entering chunk c, to slot c / every
             const int every = CKPT == 1 ? 1 : a.ckpt_every;
             const int64_t nslot = ((int64_t)NC + every - 1) / every + 1;
             if (CKPT == 1 || c % every == 0) {
@@ -409,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
                     a.state_out[idx] = S[j][mt][e];
                 }
             }
-    if constexpr (CKPT != 0) {   // the final state in the last checkpoint slot
+    if constexpr (CKPT == 1 || CKPT == 2) {   // the final state in the last checkpoint slot
         const int every = CKPT == 1 ? 1 : a.ckpt_every;
         const int64_t nslot = ((int64_t)NC + every - 1) / every + 1;
         float* dst = a.states + ((size_t)bh * nslot + nslot - 1) * DK * DK + col0 + n;
@@ -465,7 +475,11 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_scan(bool bf16, int dk, bool summary, const ScanArgs& a, hipStream_t s) {
-    if (a.states && a.ckpt_every == 1) {   // the state entering every chunk (the backward pass)
+    if (a.states && a.states_tiled) {   // the state entering every chunk, for the backward pass
+        if (bf16) return dk == 128 ? launch_scan_t<__bf16, 128, false, 3>(a, s) : launch_scan_t<__bf16, 64, false, 3>(a, s);
+        return dk == 128 ? launch_scan_t<float, 128, false, 3>(a, s) : launch_scan_t<float, 64, false, 3>(a, s);
+    }
+    if (a.states && a.ckpt_every == 1) {   // checkpoints at every chunk
         if (bf16) return dk == 128 ? launch_scan_t<__bf16, 128, false, 1>(a, s) : launch_scan_t<__bf16, 64, false, 1>(a, s);
         return dk == 128 ? launch_scan_t<float, 128, false, 1>(a, s) : launch_scan_t<float, 64, false, 1>(a, s);
     }
