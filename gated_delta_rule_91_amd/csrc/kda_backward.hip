@@ -509,14 +509,27 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         st4(sEG + i * LDK + ch, lam);
     }
     __syncthreads();
-    // q^ again after the column loop (its LDS rows hold the state blocks meanwhile)
-    auto load_qhat = [&]() {
+    // q^ (and, with bf16 operands at d_k = 128, k^) again after the column
+    // loop: their LDS rows hold other operands meanwhile.  Recomputed from the
+    // inputs and the stored reciprocal norms, so the values are the same.
+    // The loads are issued first and the products stored later, so that
+    // other work covers their latency.
+    typedef typename Raw4<E>::type RawPiece;
+    auto issue_hat = [&](const E* xp, RawPiece* raw) {
+#pragma unroll
+        for (int jj = 0; jj < NPC; ++jj) {
+            int i = (t + jj * NTH) / TPL;
+            // recomputed here rather than kept live from the input phase (that spills)
+            asm volatile("" : "+v"(i));
+            raw[jj] = *reinterpret_cast<const RawPiece*>(xp + rowi(i) * DK + ((t + jj * NTH) % TPL) * 4);
+        }
+    };
+    auto store_hat = [&](const RawPiece* raw, float* dst, const float* rn) {
 #pragma unroll
         for (int jj = 0; jj < NPC; ++jj) {
             const int idx = t + jj * NTH;
             const int i = idx / TPL, ch = (idx % TPL) * 4;
-            const f32x4 x = ld4(qp + rowi(i) * DK + ch);
-            st4(sQ + i * LDK + ch, i < nvalid ? x * sRq[i] : f32x4{0.f, 0.f, 0.f, 0.f});
+            st4(dst + i * LDK + ch, i < nvalid ? widen4(raw[jj]) * rn[i] : f32x4{0.f, 0.f, 0.f, 0.f});
         }
     };
     if (t < DK) {   // e^gamma: cumulative log-decay of channel t (the column read first, then summed)
@@ -692,177 +705,327 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         }
     }
     Pre pre = fetch(0);
-    for (int vb = 0; vb < DV / NB; ++vb) {
-        const int col0 = NB * vb;
-        // S0 and dS, this block's columns, to LDS (q^ is reloaded after the loop)
+    if constexpr (BF && DK == 128) {
+        // bf16 operand copies laid out so that every MFMA fragment is one
+        // 8- or 16-byte LDS read (the fp32 tiles were read one element at a
+        // time down their columns): over q^ the state blocks, transposed for
+        // the products that contract over channels and as they are for the
+        // ones that contract over the block's columns; over k^ (reloaded after
+        // the loop) T, P^T and T^T; over the fp32 value tiles the value-side
+        // operands.  Every value is the bf16 rounding the fp32 version used.
+        constexpr int LDT = DK + 8;    // [NB][DK] transposed state blocks
+        constexpr int LDN = NB + 8;    // [rows][NB] blocks as they are
+        constexpr int LDM = C + 8;     // [C][C] matrices and [NB][C] transposed value blocks
+        static_assert(2 * NB * LDT * 2 + 2 * DK * LDN * 2 <= C * LDK * 4, "state blocks fit over q^");
+        static_assert(3 * C * LDM * 2 <= C * LDK * 4, "T, P^T, T^T fit over k^");
+        static_assert(3 * NB * LDM * 2 + 4 * C * LDN * 2 <= 4 * C * LDB * 4, "value blocks fit over the fp32 value tiles");
+        __bf16* bS0T = reinterpret_cast<__bf16*>(sQ);          // [NB][LDT]: S0 block, transposed
+        __bf16* bDST = bS0T + NB * LDT;                        // [NB][LDT]: dS block, transposed
+        __bf16* bS0 = bDST + NB * LDT;                         // [DK][LDN]
+        __bf16* bDS = bS0 + DK * LDN;                          // [DK][LDN]
+        __bf16* bT = reinterpret_cast<__bf16*>(sK);            // [C][LDM]: T
+        __bf16* bPT = bT + C * LDM;                            // [C][LDM]: P^T
+        __bf16* bTT = bPT + C * LDM;                           // [C][LDM]: T^T
+        __bf16* bBRT = reinterpret_cast<__bf16*>(sR);          // [NB][LDM]: (diag(beta) R)^T
+        __bf16* bDOT = bBRT + NB * LDM;                        // [NB][LDM]: dO^T
+        __bf16* bDUT = bDOT + NB * LDM;                        // [NB][LDM]: dU^T
+        __bf16* bU = bDUT + NB * LDM;                          // [C][LDN]: U
+        __bf16* bDO = bU + C * LDN;                            // [C][LDN]: dO
+        __bf16* bDUt = bDO + C * LDN;                          // [C][LDN]: dU~
+        __bf16* bBDUt = bDUt + C * LDN;                        // [C][LDN]: -diag(beta) dU~
+        auto rd8 = [](const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); };
+        auto rd4 = [](const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); };
+        auto neg4 = [](bf16x4 x) {   // exact sign flip
+            typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+            return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u16x4, x) ^ (uint16_t)0x8000);
+        };
+        __syncthreads();   // every wave has its k^ fragments (afr); k^ is overwritten next
+        for (int idx = t; idx < C * C; idx += NTH) {
+            const int i = idx / C, j = idx % C;
+            bT[i * LDM + j] = (__bf16)sT[i * LDC + j];
+            bPT[i * LDM + j] = (__bf16)sP[j * LDC + i];
+            bTT[i * LDM + j] = (__bf16)sT[j * LDC + i];
+        }
+        for (int vb = 0; vb < DV / NB; ++vb) {
+            const int col0 = NB * vb;
+            // S0 and dS, this block's columns: rows 4 (idx / 16) .. + 3 of column idx % 16 per piece
 #pragma unroll
-        for (int j = 0; j < NSI; ++j) {
-            const int idx = t + j * NTH;
-            if (idx < DK * NB / 4) {
-                const int r0 = 4 * (idx / 16), c = idx % 16;
-                const f32x4 x = pre.s[j], y = pre.d[j];
+            for (int j = 0; j < NSI; ++j) {
+                const int idx = t + j * NTH;
+                if (idx < DK * NB / 4) {
+                    const int r0 = 4 * (idx / 16), c = idx % 16;
+                    const f32x4 x = pre.s[j], y = pre.d[j];
+                    *reinterpret_cast<bf16x4*>(bS0T + c * LDT + r0) = to_bf16x4(x);
+                    *reinterpret_cast<bf16x4*>(bDST + c * LDT + r0) = to_bf16x4(y);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bS0[(r0 + e) * LDN + c] = (__bf16)x[e];
+                        bDS[(r0 + e) * LDN + c] = (__bf16)y[e];
+                    }
+                    rowp[j] += x * y;
+                }
+            }
+            const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
+            pre = fetch(vb + 1);
+            __syncthreads();
+            f32x4 rr = {0.f, 0.f, 0.f, 0.f};   // half 0: R, kept for dbeta
+            f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
+            if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rr[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
+#pragma unroll
+                for (int s = 0; s < NKF; ++s) rr = mma_bf16x32(afr[s], rd8(bS0T + n * LDT + 32 * s + 8 * g), rr);
+                f32x4 br;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) br[e] = sBeta[16 * w4 + 4 * g + e] * rr[e];
+                *reinterpret_cast<bf16x4*>(bBRT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(br);
+            } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
+                f32x4 dov;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sS0[(r0 + e) * LDSB + c] = x[e];
-                    sDS[(r0 + e) * LDSB + c] = y[e];
+                    const int i = 16 * w4 + 4 * g + e;
+                    const size_t ri = rowi(i) * DV + col0 + n;
+                    const float dy = cA[e];
+                    const float sg = sigmoidf_(cB[e]);
+                    dov[e] = i < nvalid ? dy * sg : 0.f;
+                    bDO[i * LDN + n] = (__bf16)dov[e];
+                    if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
                 }
-                rowp[j] += x * y;
+                *reinterpret_cast<bf16x4*>(bDOT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(dov);
+#pragma unroll
+                for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], rd8(bDST + n * LDT + 32 * s + 8 * g), du);
             }
-        }
-        const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
-        pre = fetch(vb + 1);
-        __syncthreads();
-        f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
-        if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
-            f32x4 r;
+            __syncthreads();
+            if (half == 0) {   // U = T diag(beta) R (T lower triangular: its tiles past block w4 are zero)
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
-            if constexpr (BF) {
+                for (int s = 0; s < 2; ++s)
+                    u = mma_bf16x32(rd8(bT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bBRT + n * LDM + 32 * s + 8 * g), u);
 #pragma unroll
-                for (int s = 0; s < NKF; ++s) r = mma_bf16x32(afr[s], col8(sS0 + (32 * s + 8 * g) * LDSB + n, LDSB), r);
-            } else {
-#pragma unroll 8
-                for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w4 + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
+                for (int e = 0; e < 4; ++e) bU[(16 * w4 + 4 * g + e) * LDN + n] = (__bf16)u[e];
+            } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    du = mma_bf16x32(rd8(bPT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDOT + n * LDM + 32 * s + 8 * g), du);
+                *reinterpret_cast<bf16x4*>(bDUT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(du);
             }
+            __syncthreads();
+            if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
+                f32x4 dut = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sR[(16 * w4 + 4 * g + e) * LDB + n] = r[e];
-        } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
+                for (int s = 0; s < 2; ++s)
+                    dut = mma_bf16x32(rd8(bTT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDUT + n * LDM + 32 * s + 8 * g), dut);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w4 + 4 * g + e;
-                const size_t ri = rowi(i) * DV + col0 + n;
-                const float dy = cA[e];
-                const float sg = sigmoidf_(cB[e]);
-                sDO[i * LDB + n] = i < nvalid ? dy * sg : 0.f;
-                if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
-            }
-            if constexpr (BF) {
-#pragma unroll
-                for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], col8(sDS + (32 * s + 8 * g) * LDSB + n, LDSB), du);
-            } else {
-#pragma unroll 8
-                for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
-            }
-        }
-        __syncthreads();
-        if (half == 0) {   // U = T diag(beta) R (T lower triangular)
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF) {   // 32-token k-blocks 0, 1 (T's tiles above block w4 are zero)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int j0 = 32 * s + 8 * g;
-                    bf16x8 bb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bb[e] = (__bf16)(sBeta[j0 + e] * sR[(j0 + e) * LDB + n]);
-                    const float* ta = sT + (16 * w4 + n) * LDC + j0;
-                    u = mma_bf16x32(to_bf16x8(ld4s(ta), ld4s(ta + 4)), bb, u);
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * w4 + 4 * g + e;
+                    if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
+                    dbp[e] += dut[e] * rr[e];
+                    bDUt[i * LDN + n] = (__bf16)dut[e];
+                    bBDUt[i * LDN + n] = (__bf16)(-sBeta[i] * dut[e]);
                 }
-            } else {
-                for (int s = 0; s < 4 * (w4 + 1); ++s)
-                    u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
+            } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
+                const bf16x4 ao = rd4(bDO + (16 * w4 + n) * LDN + 4 * g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(ao, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
             }
+            __syncthreads();
+            if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
+                const bf16x4 am = neg4(rd4(bDUt + (16 * w4 + n) * LDN + 4 * g));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
-        } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
-            if constexpr (BF) {   // 32-token k-blocks 0, 1 (P^T's tiles below block w4 are zero)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
-                    du = mma_bf16x32(col8(sP + j0 * LDC + ci, LDC), col8(sDO + j0 * LDB + n, LDB), du);
-                }
-            } else {
-                for (int s = 4 * w4; s < NKC; ++s)
-                    du = mma_f32(sP[(4 * s + g) * LDC + 16 * w4 + n], sDO[(4 * s + g) * LDB + n], du);
+                for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(am, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = du[e];
-        }
-        __syncthreads();
-        f32x4 dut = {0.f, 0.f, 0.f, 0.f};
-        if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
-            if constexpr (BF) {   // 32-token k-blocks 0, 1 (T^T's tiles below block w4 are zero)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
-                    dut = mma_bf16x32(col8(sT + j0 * LDC + ci, LDC), col8(sDU + j0 * LDB + n, LDB), dut);
-                }
-            } else {
-                for (int s = 4 * w4; s < NKC; ++s)
-                    dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w4 + n], sDU[(4 * s + g) * LDB + n], dut);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {   // dU~ replaces R in LDS (each element by the lane that read it)
-                const int i = 16 * w4 + 4 * g + e;
-                if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
-                dbp[e] += dut[e] * sR[i * LDB + n];
-                sR[i * LDB + n] = dut[e];
-            }
-        } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
-            const bf16x4 ao = to_bf16x4(ld4s(sDO + (16 * w4 + n) * LDB + 4 * g));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                {
-                    if constexpr (BF) {
-                        dMP[j] = mma_bf16(ao, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
-                    } else {
-#pragma unroll
-                        for (int s = 0; s < NB / 4; ++s)
-                            dMP[j] = mma_f32(sDO[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
-                                             dMP[j]);
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
-            const bf16x4 am = to_bf16x4(-ld4s(sR + (16 * w4 + n) * LDB + 4 * g));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                {
-                    if constexpr (BF) {
-                        dMP[j] = mma_bf16(am, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
-                    } else {
-#pragma unroll
-                        for (int s = 0; s < NB / 4; ++s)
-                            dMP[j] = mma_f32(-sR[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
-                                             dMP[j]);
-                    }
-                }
-            }
-        }
-        // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles)
-        if constexpr (BF) {   // the block's 16 value columns are one bf16 k-step
-            const int ra = (16 * w4 + n) * LDB + 4 * g;
-            const bf16x4 ao = to_bf16x4(ld4s(sDO + ra));
-            const bf16x4 ar = to_bf16x4(-sBeta[16 * w4 + n] * ld4s(sR + ra));
-            const bf16x4 au = to_bf16x4(ld4s(sU + ra));
+            // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles; the
+            // block's 16 value columns are one bf16 k-step)
+            const int ra = (16 * w4 + n) * LDN + 4 * g;
+            const bf16x4 ao = rd4(bDO + ra), ar = rd4(bBDUt + ra), au = rd4(bU + ra);
 #pragma unroll
             for (int c2 = 0; c2 < NTH2; ++c2) {
-                const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * g;
-                const bf16x4 b0 = to_bf16x4(ld4s(sS0 + si)), b1 = to_bf16x4(ld4s(sDS + si));
+                const int si = (16 * (ct0 + c2) + n) * LDN + 4 * g;
+                const bf16x4 b0 = rd4(bS0 + si), b1 = rd4(bDS + si);
                 aQ[c2] = mma_bf16(ao, b0, aQ[c2]);
                 aK[c2] = mma_bf16(ar, b0, aK[c2]);
                 aE[c2] = mma_bf16(au, b1, aE[c2]);
             }
-        } else
-#pragma unroll
-        for (int s = 0; s < NB / 4; ++s) {
-            const float ao = sDO[(16 * w4 + n) * LDB + 4 * s + g];
-            const float ar = -sBeta[16 * w4 + n] * sR[(16 * w4 + n) * LDB + 4 * s + g];
-            const float au = sU[(16 * w4 + n) * LDB + 4 * s + g];
-#pragma unroll
-            for (int c2 = 0; c2 < NTH2; ++c2) {
-                const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * s + g;
-                const float b0 = sS0[si], b1 = sDS[si];
-                aQ[c2] = mma_f32(ao, b0, aQ[c2]);
-                aK[c2] = mma_f32(ar, b0, aK[c2]);
-                aE[c2] = mma_f32(au, b1, aE[c2]);
-            }
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        for (int vb = 0; vb < DV / NB; ++vb) {
+            const int col0 = NB * vb;
+            // S0 and dS, this block's columns, to LDS (q^ is reloaded after the loop)
+    #pragma unroll
+            for (int j = 0; j < NSI; ++j) {
+                const int idx = t + j * NTH;
+                if (idx < DK * NB / 4) {
+                    const int r0 = 4 * (idx / 16), c = idx % 16;
+                    const f32x4 x = pre.s[j], y = pre.d[j];
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sS0[(r0 + e) * LDSB + c] = x[e];
+                        sDS[(r0 + e) * LDSB + c] = y[e];
+                    }
+                    rowp[j] += x * y;
+                }
+            }
+            const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
+            pre = fetch(vb + 1);
+            __syncthreads();
+            f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
+            if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
+                f32x4 r;
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
+                if constexpr (BF) {
+    #pragma unroll
+                    for (int s = 0; s < NKF; ++s) r = mma_bf16x32(afr[s], col8(sS0 + (32 * s + 8 * g) * LDSB + n, LDSB), r);
+                } else {
+    #pragma unroll 8
+                    for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w4 + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
+                }
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) sR[(16 * w4 + 4 * g + e) * LDB + n] = r[e];
+            } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * w4 + 4 * g + e;
+                    const size_t ri = rowi(i) * DV + col0 + n;
+                    const float dy = cA[e];
+                    const float sg = sigmoidf_(cB[e]);
+                    sDO[i * LDB + n] = i < nvalid ? dy * sg : 0.f;
+                    if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
+                }
+                if constexpr (BF) {
+    #pragma unroll
+                    for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], col8(sDS + (32 * s + 8 * g) * LDSB + n, LDSB), du);
+                } else {
+    #pragma unroll 8
+                    for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
+                }
+            }
+            __syncthreads();
+            if (half == 0) {   // U = T diag(beta) R (T lower triangular)
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BF) {   // 32-token k-blocks 0, 1 (T's tiles above block w4 are zero)
+    #pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int j0 = 32 * s + 8 * g;
+                        bf16x8 bb;
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e) bb[e] = (__bf16)(sBeta[j0 + e] * sR[(j0 + e) * LDB + n]);
+                        const float* ta = sT + (16 * w4 + n) * LDC + j0;
+                        u = mma_bf16x32(to_bf16x8(ld4s(ta), ld4s(ta + 4)), bb, u);
+                    }
+                } else {
+                    for (int s = 0; s < 4 * (w4 + 1); ++s)
+                        u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
+                }
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
+            } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
+                if constexpr (BF) {   // 32-token k-blocks 0, 1 (P^T's tiles below block w4 are zero)
+    #pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
+                        du = mma_bf16x32(col8(sP + j0 * LDC + ci, LDC), col8(sDO + j0 * LDB + n, LDB), du);
+                    }
+                } else {
+                    for (int s = 4 * w4; s < NKC; ++s)
+                        du = mma_f32(sP[(4 * s + g) * LDC + 16 * w4 + n], sDO[(4 * s + g) * LDB + n], du);
+                }
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = du[e];
+            }
+            __syncthreads();
+            f32x4 dut = {0.f, 0.f, 0.f, 0.f};
+            if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
+                if constexpr (BF) {   // 32-token k-blocks 0, 1 (T^T's tiles below block w4 are zero)
+    #pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
+                        dut = mma_bf16x32(col8(sT + j0 * LDC + ci, LDC), col8(sDU + j0 * LDB + n, LDB), dut);
+                    }
+                } else {
+                    for (int s = 4 * w4; s < NKC; ++s)
+                        dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w4 + n], sDU[(4 * s + g) * LDB + n], dut);
+                }
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {   // dU~ replaces R in LDS (each element by the lane that read it)
+                    const int i = 16 * w4 + 4 * g + e;
+                    if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
+                    dbp[e] += dut[e] * sR[i * LDB + n];
+                    sR[i * LDB + n] = dut[e];
+                }
+            } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
+                const bf16x4 ao = to_bf16x4(ld4s(sDO + (16 * w4 + n) * LDB + 4 * g));
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    {
+                        if constexpr (BF) {
+                            dMP[j] = mma_bf16(ao, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
+                        } else {
+    #pragma unroll
+                            for (int s = 0; s < NB / 4; ++s)
+                                dMP[j] = mma_f32(sDO[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
+                                                 dMP[j]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
+                const bf16x4 am = to_bf16x4(-ld4s(sR + (16 * w4 + n) * LDB + 4 * g));
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    {
+                        if constexpr (BF) {
+                            dMP[j] = mma_bf16(am, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
+                        } else {
+    #pragma unroll
+                            for (int s = 0; s < NB / 4; ++s)
+                                dMP[j] = mma_f32(-sR[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
+                                                 dMP[j]);
+                        }
+                    }
+                }
+            }
+            // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles)
+            if constexpr (BF) {   // the block's 16 value columns are one bf16 k-step
+                const int ra = (16 * w4 + n) * LDB + 4 * g;
+                const bf16x4 ao = to_bf16x4(ld4s(sDO + ra));
+                const bf16x4 ar = to_bf16x4(-sBeta[16 * w4 + n] * ld4s(sR + ra));
+                const bf16x4 au = to_bf16x4(ld4s(sU + ra));
+    #pragma unroll
+                for (int c2 = 0; c2 < NTH2; ++c2) {
+                    const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * g;
+                    const bf16x4 b0 = to_bf16x4(ld4s(sS0 + si)), b1 = to_bf16x4(ld4s(sDS + si));
+                    aQ[c2] = mma_bf16(ao, b0, aQ[c2]);
+                    aK[c2] = mma_bf16(ar, b0, aK[c2]);
+                    aE[c2] = mma_bf16(au, b1, aE[c2]);
+                }
+            } else
+    #pragma unroll
+            for (int s = 0; s < NB / 4; ++s) {
+                const float ao = sDO[(16 * w4 + n) * LDB + 4 * s + g];
+                const float ar = -sBeta[16 * w4 + n] * sR[(16 * w4 + n) * LDB + 4 * s + g];
+                const float au = sU[(16 * w4 + n) * LDB + 4 * s + g];
+    #pragma unroll
+                for (int c2 = 0; c2 < NTH2; ++c2) {
+                    const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * s + g;
+                    const float b0 = sS0[si], b1 = sDS[si];
+                    aQ[c2] = mma_f32(ao, b0, aQ[c2]);
+                    aK[c2] = mma_f32(ar, b0, aK[c2]);
+                    aE[c2] = mma_f32(au, b1, aE[c2]);
+                }
+            }
+            __syncthreads();
+        }
     }
 
-    // rowsum(S0 * dS): the 16 columns of a row group sit in 16 adjacent lanes; q^ back over the state blocks
+    // q^ back over the state blocks: the loads now, the stores after phase 5
+    // (k^, where it was overwritten, after phase 5: both at once spill)
+    constexpr bool KHAT = BF && DK == 128;
+    RawPiece qraw[NPC];
+    issue_hat(qp, qraw);
+    // rowsum(S0 * dS): the 16 columns of a row group sit in 16 adjacent lanes
 #pragma unroll
     for (int j = 0; j < NSI; ++j) {
         f32x4 x = rowp[j];
@@ -873,7 +1036,6 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         const int idx = t + j * NTH;
         if (idx < DK * NB / 4 && (idx & 15) == 0) st4(sDGC + 4 * DK + 4 * (idx / 16), x);
     }
-    load_qhat();
 
     // ---- 5: dbeta, dA -> sT (half 0); dP -> sP (half 1) ----
     if (half == 0) {
@@ -902,6 +1064,12 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             if (half == 0) sT[i * LDC + jj] = (j <= w4 && jj < i) ? sBeta[i] * dMP[j][e] : 0.f;   // dA
             else sP[i * LDC + jj] = (j <= w4 && jj <= i) ? dMP[j][e] : 0.f;                      // dP
         }
+    store_hat(qraw, sQ, sRq);
+    if constexpr (KHAT) {
+        RawPiece kraw[NPC];
+        issue_hat(kp, kraw);
+        store_hat(kraw, sK, sRk);
+    }
     __syncthreads();
 
     // ---- 6: dQt += dP Kh, dKt += dA Kh, dKh = dP^T Qt + dA^T Kt ----
@@ -983,25 +1151,36 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             }
         }
         __syncthreads();
-        E* dkp = reinterpret_cast<E*>(a.dk);
-        E* dqp = reinterpret_cast<E*>(a.dq);
+        // a lane holds four tokens of one channel: dk and dq replace k^ and q^
+        // in LDS (each element by the lane that read it), then go out as
+        // whole 8-channel pieces of a token
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * w4 + 4 * g + e;
-            if (i < nvalid) {
-                const float nk = sNk[i], nq = sNq[i], rk = sRk[i], rq = sRq[i];
-                const float kdi = sXD[i] + sXD[2 * C + i], qdi = sXD[C + i] + sXD[3 * C + i];
-                const size_t ri = rowi(i) * DK;
+            const float nk = sNk[i], nq = sNq[i], rk = sRk[i], rq = sRq[i];
+            const float kdi = sXD[i] + sXD[2 * C + i], qdi = sXD[C + i] + sXD[3 * C + i];
 #pragma unroll
-                for (int c2 = 0; c2 < NTH2; ++c2) {
-                    const int ch = 16 * (ct0 + c2) + n;
-                    // rk = 1 / max(|k|, 1e-6): below the floor the normaliser is the constant 1e6
-                    const float dkx = (nk < 1e-6f ? aK[c2][e] : aK[c2][e] - sK[i * LDK + ch] * kdi) * rk;
-                    const float dqx = (nq < 1e-6f ? aQ[c2][e] : aQ[c2][e] - sQ[i * LDK + ch] * qdi) * rq;
-                    dkp[ri + ch] = from_f32<E>(dkx);
-                    dqp[ri + ch] = from_f32<E>(dqx);
-                }
+            for (int c2 = 0; c2 < NTH2; ++c2) {
+                const int ch = 16 * (ct0 + c2) + n;
+                float* kk = sK + i * LDK + ch;
+                float* qq = sQ + i * LDK + ch;
+                // rk = 1 / max(|k|, 1e-6): below the floor the normaliser is the constant 1e6
+                const float dkx = (nk < 1e-6f ? aK[c2][e] : aK[c2][e] - *kk * kdi) * rk;
+                const float dqx = (nq < 1e-6f ? aQ[c2][e] : aQ[c2][e] - *qq * qdi) * rq;
+                *kk = dkx;
+                *qq = dqx;
             }
+        }
+        __syncthreads();
+        E* dkp = reinterpret_cast<E*>(a.dk);
+        E* dqp = reinterpret_cast<E*>(a.dq);
+        for (int idx = t; idx < nvalid * (DK / 8); idx += NTH) {
+            const int i = idx / (DK / 8), ch = (idx % (DK / 8)) * 8;
+            const size_t ri = rowi(i) * DK + ch;
+            st4(dkp + ri, ld4s(sK + i * LDK + ch));
+            st4(dkp + ri + 4, ld4s(sK + i * LDK + ch + 4));
+            st4(dqp + ri, ld4s(sQ + i * LDK + ch));
+            st4(dqp + ri + 4, ld4s(sQ + i * LDK + ch + 4));
         }
     }
     // ---- 9: dgamma to LDS (over dP and dA, read for the last time in phase 6) ----

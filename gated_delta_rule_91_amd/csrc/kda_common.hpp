@@ -85,6 +85,13 @@ __device__ __forceinline__ typename MM<E>::frag ld_frag(const E* base, int ld, i
 }
 
 // Four consecutive elements (8 B for bf16, 16 B for fp32) <-> fp32x4.
+// Four consecutive elements kept as loaded; widened to fp32 only where used,
+// so no conversion sits right behind its load.
+template <typename E> struct Raw4 { typedef f32x4 type; };
+template <> struct Raw4<__bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 widen4(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+__device__ __forceinline__ f32x4 widen4(f32x4 x) { return x; }
+
 __device__ __forceinline__ f32x4 ld4(const __bf16* p) {
     bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
     return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};

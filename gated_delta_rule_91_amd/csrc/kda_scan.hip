@@ -46,13 +46,6 @@ namespace {
 
 constexpr int kXcds = 8;
 
-// Four consecutive elements kept as loaded; widened to fp32 only where used,
-// so no conversion sits right behind its load.
-template <typename E> struct Raw4 { typedef f32x4 type; };
-template <> struct Raw4<__bf16> { typedef bf16x4 type; };
-__device__ __forceinline__ f32x4 widen4(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
-__device__ __forceinline__ f32x4 widen4(f32x4 x) { return x; }
-
 template <typename E, int DK, int NTW>
 struct ChunkOps {
     using M = MM<E>;
