@@ -37,6 +37,8 @@
 //                             gradient from S0, dS and the chunk's inputs
 //                             (bf16 MFMA for most products with bf16 I/O,
 //                             fp32 MFMA otherwise)
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -746,108 +748,117 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             bPT[i * LDM + j] = (__bf16)sP[j * LDC + i];
             bTT[i * LDM + j] = (__bf16)sT[j * LDC + i];
         }
-        for (int vb = 0; vb < DV / NB; ++vb) {
-            const int col0 = NB * vb;
-            // S0 and dS, this block's columns: rows 4 (idx / 16) .. + 3 of column idx % 16 per piece
-#pragma unroll
-            for (int j = 0; j < NSI; ++j) {
-                const int idx = t + j * NTH;
-                if (idx < DK * NB / 4) {
-                    const int r0 = 4 * (idx / 16), c = idx % 16;
-                    const f32x4 x = pre.s[j], y = pre.d[j];
-                    *reinterpret_cast<bf16x4*>(bS0T + c * LDT + r0) = to_bf16x4(x);
-                    *reinterpret_cast<bf16x4*>(bDST + c * LDT + r0) = to_bf16x4(y);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bS0[(r0 + e) * LDN + c] = (__bf16)x[e];
-                        bDS[(r0 + e) * LDN + c] = (__bf16)y[e];
+        // FULL: the chunk holds C tokens, so the dv and dg stores are
+        // unconditional (a store under a branch leaves the compiler unsure how
+        // many accesses are in flight, and its later waits then also wait for
+        // those stores and for the next block's inputs)
+        auto column_loop = [&](auto full) {
+            constexpr bool FULL = decltype(full)::value;
+            for (int vb = 0; vb < DV / NB; ++vb) {
+                const int col0 = NB * vb;
+                // S0 and dS, this block's columns: rows 4 (idx / 16) .. + 3 of column idx % 16 per piece
+    #pragma unroll
+                for (int j = 0; j < NSI; ++j) {
+                    const int idx = t + j * NTH;
+                    if (idx < DK * NB / 4) {
+                        const int r0 = 4 * (idx / 16), c = idx % 16;
+                        const f32x4 x = pre.s[j], y = pre.d[j];
+                        *reinterpret_cast<bf16x4*>(bS0T + c * LDT + r0) = to_bf16x4(x);
+                        *reinterpret_cast<bf16x4*>(bDST + c * LDT + r0) = to_bf16x4(y);
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            bS0[(r0 + e) * LDN + c] = (__bf16)x[e];
+                            bDS[(r0 + e) * LDN + c] = (__bf16)y[e];
+                        }
+                        rowp[j] += x * y;
                     }
-                    rowp[j] += x * y;
                 }
-            }
-            const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
-            pre = fetch(vb + 1);
-            __syncthreads();
-            f32x4 rr = {0.f, 0.f, 0.f, 0.f};   // half 0: R, kept for dbeta
-            f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
-            if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) rr[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
-#pragma unroll
-                for (int s = 0; s < NKF; ++s) rr = mma_bf16x32(afr[s], rd8(bS0T + n * LDT + 32 * s + 8 * g), rr);
-                f32x4 br;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) br[e] = sBeta[16 * w4 + 4 * g + e] * rr[e];
-                *reinterpret_cast<bf16x4*>(bBRT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(br);
-            } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
-                f32x4 dov;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * w4 + 4 * g + e;
-                    const size_t ri = rowi(i) * DV + col0 + n;
-                    const float dy = cA[e];
-                    const float sg = sigmoidf_(cB[e]);
-                    dov[e] = i < nvalid ? dy * sg : 0.f;
-                    bDO[i * LDN + n] = (__bf16)dov[e];
-                    if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
+                const f32x4 cA = pre.a, cB = pre.b, cC = pre.c;
+                pre = fetch(vb + 1);
+                __syncthreads();
+                f32x4 rr = {0.f, 0.f, 0.f, 0.f};   // half 0: R, kept for dbeta
+                f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
+                if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) rr[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
+    #pragma unroll
+                    for (int s = 0; s < NKF; ++s) rr = mma_bf16x32(afr[s], rd8(bS0T + n * LDT + 32 * s + 8 * g), rr);
+                    f32x4 br;
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) br[e] = sBeta[16 * w4 + 4 * g + e] * rr[e];
+                    *reinterpret_cast<bf16x4*>(bBRT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(br);
+                } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
+                    f32x4 dov;
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * w4 + 4 * g + e;
+                        const size_t ri = rowi(i) * DV + col0 + n;
+                        const float dy = cA[e];
+                        const float sg = sigmoidf_(cB[e]);
+                        dov[e] = i < nvalid ? dy * sg : 0.f;
+                        bDO[i * LDN + n] = (__bf16)dov[e];
+                        if (FULL || i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
+                    }
+                    *reinterpret_cast<bf16x4*>(bDOT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(dov);
+    #pragma unroll
+                    for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], rd8(bDST + n * LDT + 32 * s + 8 * g), du);
                 }
-                *reinterpret_cast<bf16x4*>(bDOT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(dov);
-#pragma unroll
-                for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], rd8(bDST + n * LDT + 32 * s + 8 * g), du);
-            }
-            __syncthreads();
-            if (half == 0) {   // U = T diag(beta) R (T lower triangular: its tiles past block w4 are zero)
-                f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    u = mma_bf16x32(rd8(bT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bBRT + n * LDM + 32 * s + 8 * g), u);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bU[(16 * w4 + 4 * g + e) * LDN + n] = (__bf16)u[e];
-            } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    du = mma_bf16x32(rd8(bPT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDOT + n * LDM + 32 * s + 8 * g), du);
-                *reinterpret_cast<bf16x4*>(bDUT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(du);
-            }
-            __syncthreads();
-            if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
-                f32x4 dut = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    dut = mma_bf16x32(rd8(bTT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDUT + n * LDM + 32 * s + 8 * g), dut);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * w4 + 4 * g + e;
-                    if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
-                    dbp[e] += dut[e] * rr[e];
-                    bDUt[i * LDN + n] = (__bf16)dut[e];
-                    bBDUt[i * LDN + n] = (__bf16)(-sBeta[i] * dut[e]);
+                __syncthreads();
+                if (half == 0) {   // U = T diag(beta) R (T lower triangular: its tiles past block w4 are zero)
+                    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        u = mma_bf16x32(rd8(bT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bBRT + n * LDM + 32 * s + 8 * g), u);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) bU[(16 * w4 + 4 * g + e) * LDN + n] = (__bf16)u[e];
+                } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
+    #pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        du = mma_bf16x32(rd8(bPT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDOT + n * LDM + 32 * s + 8 * g), du);
+                    *reinterpret_cast<bf16x4*>(bDUT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(du);
                 }
-            } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
-                const bf16x4 ao = rd4(bDO + (16 * w4 + n) * LDN + 4 * g);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(ao, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
+                __syncthreads();
+                if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
+                    f32x4 dut = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        dut = mma_bf16x32(rd8(bTT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDUT + n * LDM + 32 * s + 8 * g), dut);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * w4 + 4 * g + e;
+                        if (FULL || i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
+                        dbp[e] += dut[e] * rr[e];
+                        bDUt[i * LDN + n] = (__bf16)dut[e];
+                        bBDUt[i * LDN + n] = (__bf16)(-sBeta[i] * dut[e]);
+                    }
+                } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
+                    const bf16x4 ao = rd4(bDO + (16 * w4 + n) * LDN + 4 * g);
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(ao, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
+                }
+                __syncthreads();
+                if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
+                    const bf16x4 am = neg4(rd4(bDUt + (16 * w4 + n) * LDN + 4 * g));
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(am, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
+                }
+                // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles; the
+                // block's 16 value columns are one bf16 k-step)
+                const int ra = (16 * w4 + n) * LDN + 4 * g;
+                const bf16x4 ao = rd4(bDO + ra), ar = rd4(bBDUt + ra), au = rd4(bU + ra);
+    #pragma unroll
+                for (int c2 = 0; c2 < NTH2; ++c2) {
+                    const int si = (16 * (ct0 + c2) + n) * LDN + 4 * g;
+                    const bf16x4 b0 = rd4(bS0 + si), b1 = rd4(bDS + si);
+                    aQ[c2] = mma_bf16(ao, b0, aQ[c2]);
+                    aK[c2] = mma_bf16(ar, b0, aK[c2]);
+                    aE[c2] = mma_bf16(au, b1, aE[c2]);
+                }
+                __syncthreads();
             }
-            __syncthreads();
-            if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
-                const bf16x4 am = neg4(rd4(bDUt + (16 * w4 + n) * LDN + 4 * g));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(am, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
-            }
-            // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles; the
-            // block's 16 value columns are one bf16 k-step)
-            const int ra = (16 * w4 + n) * LDN + 4 * g;
-            const bf16x4 ao = rd4(bDO + ra), ar = rd4(bBDUt + ra), au = rd4(bU + ra);
-#pragma unroll
-            for (int c2 = 0; c2 < NTH2; ++c2) {
-                const int si = (16 * (ct0 + c2) + n) * LDN + 4 * g;
-                const bf16x4 b0 = rd4(bS0 + si), b1 = rd4(bDS + si);
-                aQ[c2] = mma_bf16(ao, b0, aQ[c2]);
-                aK[c2] = mma_bf16(ar, b0, aK[c2]);
-                aE[c2] = mma_bf16(au, b1, aE[c2]);
-            }
-            __syncthreads();
-        }
+        };
+        if (nvalid == C) column_loop(std::true_type{});
+        else column_loop(std::false_type{});
     } else {
         for (int vb = 0; vb < DV / NB; ++vb) {
             const int col0 = NB * vb;
