@@ -511,11 +511,10 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         st4(sEG + i * LDK + ch, lam);
     }
     __syncthreads();
-    // q^ (and, with bf16 operands at d_k = 128, k^) again after the column
-    // loop: their LDS rows hold other operands meanwhile.  Recomputed from the
-    // inputs and the stored reciprocal norms, so the values are the same.
-    // The loads are issued first and the products stored later, so that
-    // other work covers their latency.
+    // q^ again after the column loop: its LDS rows hold the state blocks
+    // meanwhile.  Recomputed from the input and the stored reciprocal norms,
+    // so the values are the same.  The loads are issued first and the
+    // products stored later, so that other work covers their latency.
     typedef typename Raw4<E>::type RawPiece;
     auto issue_hat = [&](const E* xp, RawPiece* raw) {
 #pragma unroll
@@ -712,20 +711,21 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         // 8- or 16-byte LDS read (the fp32 tiles were read one element at a
         // time down their columns): over q^ the state blocks, transposed for
         // the products that contract over channels and as they are for the
-        // ones that contract over the block's columns; over k^ (reloaded after
-        // the loop) T, P^T and T^T; over the fp32 value tiles the value-side
-        // operands.  Every value is the bf16 rounding the fp32 version used.
+        // ones that contract over the block's columns; over the fp32 P and T
+        // (not read again before phase 5 writes dP and dA there) T, P^T and
+        // T^T; over the fp32 value tiles the value-side operands.  Every value
+        // is the bf16 rounding the fp32 version used.
         constexpr int LDT = DK + 8;    // [NB][DK] transposed state blocks
         constexpr int LDN = NB + 8;    // [rows][NB] blocks as they are
         constexpr int LDM = C + 8;     // [C][C] matrices and [NB][C] transposed value blocks
         static_assert(2 * NB * LDT * 2 + 2 * DK * LDN * 2 <= C * LDK * 4, "state blocks fit over q^");
-        static_assert(3 * C * LDM * 2 <= C * LDK * 4, "T, P^T, T^T fit over k^");
+        static_assert(3 * C * LDM * 2 <= 2 * C * LDC * 4 && LY::T == LY::P + (size_t)C * LDC * 4, "T, P^T, T^T fit over P and T");
         static_assert(3 * NB * LDM * 2 + 4 * C * LDN * 2 <= 4 * C * LDB * 4, "value blocks fit over the fp32 value tiles");
         __bf16* bS0T = reinterpret_cast<__bf16*>(sQ);          // [NB][LDT]: S0 block, transposed
         __bf16* bDST = bS0T + NB * LDT;                        // [NB][LDT]: dS block, transposed
         __bf16* bS0 = bDST + NB * LDT;                         // [DK][LDN]
         __bf16* bDS = bS0 + DK * LDN;                          // [DK][LDN]
-        __bf16* bT = reinterpret_cast<__bf16*>(sK);            // [C][LDM]: T
+        __bf16* bT = reinterpret_cast<__bf16*>(sP);            // [C][LDM]: T
         __bf16* bPT = bT + C * LDM;                            // [C][LDM]: P^T
         __bf16* bTT = bPT + C * LDM;                           // [C][LDM]: T^T
         __bf16* bBRT = reinterpret_cast<__bf16*>(sR);          // [NB][LDM]: (diag(beta) R)^T
@@ -741,12 +741,25 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
             return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u16x4, x) ^ (uint16_t)0x8000);
         };
-        __syncthreads();   // every wave has its k^ fragments (afr); k^ is overwritten next
-        for (int idx = t; idx < C * C; idx += NTH) {
-            const int i = idx / C, j = idx % C;
-            bT[i * LDM + j] = (__bf16)sT[i * LDC + j];
-            bPT[i * LDM + j] = (__bf16)sP[j * LDC + i];
-            bTT[i * LDM + j] = (__bf16)sT[j * LDC + i];
+        {   // read every source element first, then overwrite P and T
+            constexpr int NEL = C * C / NTH;
+            static_assert(C * C % NTH == 0, "whole elements per thread");
+            __bf16 xt[NEL], xp[NEL], xtt[NEL];
+#pragma unroll
+            for (int k = 0; k < NEL; ++k) {
+                const int idx = t + k * NTH, i = idx / C, j = idx % C;
+                xt[k] = (__bf16)sT[i * LDC + j];
+                xp[k] = (__bf16)sP[j * LDC + i];
+                xtt[k] = (__bf16)sT[j * LDC + i];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < NEL; ++k) {
+                const int idx = t + k * NTH, i = idx / C, j = idx % C;
+                bT[i * LDM + j] = xt[k];
+                bPT[i * LDM + j] = xp[k];
+                bTT[i * LDM + j] = xtt[k];
+            }
         }
         // FULL: the chunk holds C tokens, so the dv and dg stores are
         // unconditional (a store under a branch leaves the compiler unsure how
@@ -1032,8 +1045,6 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     }
 
     // q^ back over the state blocks: the loads now, the stores after phase 5
-    // (k^, where it was overwritten, after phase 5: both at once spill)
-    constexpr bool KHAT = BF && DK == 128;
     RawPiece qraw[NPC];
     issue_hat(qp, qraw);
     // rowsum(S0 * dS): the 16 columns of a row group sit in 16 adjacent lanes
@@ -1076,11 +1087,6 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             else sP[i * LDC + jj] = (j <= w4 && jj <= i) ? dMP[j][e] : 0.f;                      // dP
         }
     store_hat(qraw, sQ, sRq);
-    if constexpr (KHAT) {
-        RawPiece kraw[NPC];
-        issue_hat(kp, kraw);
-        store_hat(kraw, sK, sRk);
-    }
     __syncthreads();
 
     // ---- 6: dQt += dP Kh, dKt += dA Kh, dKh = dP^T Qt + dA^T Kt ----
