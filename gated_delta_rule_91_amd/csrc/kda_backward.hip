@@ -553,22 +553,37 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
 
     // ---- 2: half 0: A = Kt Kh^T (kept in registers, strictly lower) and
     // diag(beta) A -> sT; half 1: P = Qt Kh^T -> sP ----
+    // With bf16 operands, Kh = k^ e^-gamma is formed once as bf16 rows (over
+    // the value tiles, unused until the column loop), so each B fragment is
+    // one 16-byte read, and each wave's A fragments (rows of Kt or Qt) are
+    // formed once for its four products.
+    constexpr int LDH = DK + 8;
+    static_assert(C * LDH * 2 <= 4 * C * LDB * 4, "Kh fits over the value tiles");
+    const __bf16* bKh = reinterpret_cast<const __bf16*>(sR);
+    bf16x8 ag[BF ? DK / 32 : 1];
+    if constexpr (BF) {
+        for (int idx = t; idx < C * DK / 4; idx += NTH) {   // four channels of one token per step
+            const int i = idx / (DK / 4), ch = (idx % (DK / 4)) * 4;
+            *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(sR) + i * LDH + ch) =
+                to_bf16x4(ld4s(sK + i * LDK + ch) * rcp4(ld4s(sEG + i * LDK + ch)));
+        }
+        const float* xa = (half == 0 ? sK : sQ) + (16 * w4 + n) * LDK;
+        const float* ea = sEG + (16 * w4 + n) * LDK;
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const int c0 = 32 * s + 8 * g;
+            ag[s] = to_bf16x8(ld4s(xa + c0) * ld4s(ea + c0), ld4s(xa + c0 + 4) * ld4s(ea + c0 + 4));
+        }
+        __syncthreads();
+    }
     f32x4 As[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {   // tiles right of the diagonal come out masked to zero
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if constexpr (BF) {   // rows of Kt (or Qt) against rows of Kh, 32 channels per step
-            const float* xa = (half == 0 ? sK : sQ) + (16 * w4 + n) * LDK;
-            const float* ea = sEG + (16 * w4 + n) * LDK;
-            const float* kb = sK + (16 * j + n) * LDK;
-            const float* eb = sEG + (16 * j + n) * LDK;
 #pragma unroll
-            for (int s = 0; s < DK / 32; ++s) {
-                const int c0 = 32 * s + 8 * g;
-                x = mma_bf16x32(to_bf16x8(ld4s(xa + c0) * ld4s(ea + c0), ld4s(xa + c0 + 4) * ld4s(ea + c0 + 4)),
-                                to_bf16x8(ld4s(kb + c0) * rcp4(ld4s(eb + c0)), ld4s(kb + c0 + 4) * rcp4(ld4s(eb + c0 + 4))),
-                                x);
-            }
+            for (int s = 0; s < DK / 32; ++s)
+                x = mma_bf16x32(ag[s], *reinterpret_cast<const bf16x8*>(bKh + (16 * j + n) * LDH + 32 * s + 8 * g), x);
         } else if (half == 0) {
 #pragma unroll 8
             for (int s = 0; s < NKD; ++s) x = mma_f32(Kt(16 * w4 + n, 4 * s + g), Kh(16 * j + n, 4 * s + g), x);
