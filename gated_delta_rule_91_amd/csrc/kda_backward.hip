@@ -785,7 +785,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             for (int vb = 0; vb < DV / NB; ++vb) {
                 const int col0 = NB * vb;
                 // S0 and dS, this block's columns: rows 4 (idx / 16) .. + 3 of column idx % 16 per piece
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < NSI; ++j) {
                     const int idx = t + j * NTH;
                     if (idx < DK * NB / 4) {
@@ -793,7 +793,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                         const f32x4 x = pre.s[j], y = pre.d[j];
                         *reinterpret_cast<bf16x4*>(bS0T + c * LDT + r0) = to_bf16x4(x);
                         *reinterpret_cast<bf16x4*>(bDST + c * LDT + r0) = to_bf16x4(y);
-    #pragma unroll
+#pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             bS0[(r0 + e) * LDN + c] = (__bf16)x[e];
                             bDS[(r0 + e) * LDN + c] = (__bf16)y[e];
@@ -807,17 +807,17 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 f32x4 rr = {0.f, 0.f, 0.f, 0.f};   // half 0: R, kept for dbeta
                 f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
                 if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) rr[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < NKF; ++s) rr = mma_bf16x32(afr[s], rd8(bS0T + n * LDT + 32 * s + 8 * g), rr);
                     f32x4 br;
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) br[e] = sBeta[16 * w4 + 4 * g + e] * rr[e];
                     *reinterpret_cast<bf16x4*>(bBRT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(br);
                 } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
                     f32x4 dov;
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 16 * w4 + 4 * g + e;
                         const size_t ri = rowi(i) * DV + col0 + n;
@@ -828,19 +828,19 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                         if (FULL || i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
                     }
                     *reinterpret_cast<bf16x4*>(bDOT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(dov);
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], rd8(bDST + n * LDT + 32 * s + 8 * g), du);
                 }
                 __syncthreads();
                 if (half == 0) {   // U = T diag(beta) R (T lower triangular: its tiles past block w4 are zero)
                     f32x4 u = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < 2; ++s)
                         u = mma_bf16x32(rd8(bT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bBRT + n * LDM + 32 * s + 8 * g), u);
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) bU[(16 * w4 + 4 * g + e) * LDN + n] = (__bf16)u[e];
                 } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < 2; ++s)
                         du = mma_bf16x32(rd8(bPT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDOT + n * LDM + 32 * s + 8 * g), du);
                     *reinterpret_cast<bf16x4*>(bDUT + n * LDM + 16 * w4 + 4 * g) = to_bf16x4(du);
@@ -848,10 +848,10 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 __syncthreads();
                 if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
                     f32x4 dut = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < 2; ++s)
                         dut = mma_bf16x32(rd8(bTT + (16 * w4 + n) * LDM + 32 * s + 8 * g), rd8(bDUT + n * LDM + 32 * s + 8 * g), dut);
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 16 * w4 + 4 * g + e;
                         if (FULL || i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
@@ -861,20 +861,20 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     }
                 } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
                     const bf16x4 ao = rd4(bDO + (16 * w4 + n) * LDN + 4 * g);
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(ao, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
                 }
                 __syncthreads();
                 if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
                     const bf16x4 am = neg4(rd4(bDUt + (16 * w4 + n) * LDN + 4 * g));
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < 4; ++j) dMP[j] = mma_bf16(am, rd4(bU + (16 * j + n) * LDN + 4 * g), dMP[j]);
                 }
                 // dQt += dO S0^T, dKt -= (diag(beta) dU~) S0^T, dKe += U dS^T (this half's channel tiles; the
                 // block's 16 value columns are one bf16 k-step)
                 const int ra = (16 * w4 + n) * LDN + 4 * g;
                 const bf16x4 ao = rd4(bDO + ra), ar = rd4(bBDUt + ra), au = rd4(bU + ra);
-    #pragma unroll
+#pragma unroll
                 for (int c2 = 0; c2 < NTH2; ++c2) {
                     const int si = (16 * (ct0 + c2) + n) * LDN + 4 * g;
                     const bf16x4 b0 = rd4(bS0 + si), b1 = rd4(bDS + si);
@@ -891,13 +891,13 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
         for (int vb = 0; vb < DV / NB; ++vb) {
             const int col0 = NB * vb;
             // S0 and dS, this block's columns, to LDS (q^ is reloaded after the loop)
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < NSI; ++j) {
                 const int idx = t + j * NTH;
                 if (idx < DK * NB / 4) {
                     const int r0 = 4 * (idx / 16), c = idx % 16;
                     const f32x4 x = pre.s[j], y = pre.d[j];
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         sS0[(r0 + e) * LDSB + c] = x[e];
                         sDS[(r0 + e) * LDSB + c] = y[e];
@@ -911,19 +911,19 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             f32x4 du = {0.f, 0.f, 0.f, 0.f};   // half 1: Ke dS, then + P^T dO
             if (half == 0) {   // R = V - Kt S0 (rows 16 w4 ..)
                 f32x4 r;
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) r[e] = 16 * w4 + 4 * g + e < nvalid ? cA[e] : 0.f;
                 if constexpr (BF) {
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < NKF; ++s) r = mma_bf16x32(afr[s], col8(sS0 + (32 * s + 8 * g) * LDSB + n, LDSB), r);
                 } else {
-    #pragma unroll 8
+#pragma unroll 8
                     for (int s = 0; s < NKD; ++s) r = mma_f32(-Kt(16 * w4 + n, 4 * s + g), sS0[(4 * s + g) * LDSB + n], r);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) sR[(16 * w4 + 4 * g + e) * LDB + n] = r[e];
             } else {           // dO = d_out * sigmoid(g); dg = d_out * out * (1 - sigmoid(g)); Ke dS
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 16 * w4 + 4 * g + e;
                     const size_t ri = rowi(i) * DV + col0 + n;
@@ -933,10 +933,10 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     if (i < nvalid) dgp[ri] = from_f32<E>(dy * cC[e] * (1.f - sg));
                 }
                 if constexpr (BF) {
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < NKF; ++s) du = mma_bf16x32(afr[s], col8(sDS + (32 * s + 8 * g) * LDSB + n, LDSB), du);
                 } else {
-    #pragma unroll 8
+#pragma unroll 8
                     for (int s = 0; s < NKD; ++s) du = mma_f32(Ke(16 * w4 + n, 4 * s + g), sDS[(4 * s + g) * LDSB + n], du);
                 }
             }
@@ -944,11 +944,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             if (half == 0) {   // U = T diag(beta) R (T lower triangular)
                 f32x4 u = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (BF) {   // 32-token k-blocks 0, 1 (T's tiles above block w4 are zero)
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         const int j0 = 32 * s + 8 * g;
                         bf16x8 bb;
-    #pragma unroll
+#pragma unroll
                         for (int e = 0; e < 8; ++e) bb[e] = (__bf16)(sBeta[j0 + e] * sR[(j0 + e) * LDB + n]);
                         const float* ta = sT + (16 * w4 + n) * LDC + j0;
                         u = mma_bf16x32(to_bf16x8(ld4s(ta), ld4s(ta + 4)), bb, u);
@@ -957,11 +957,11 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     for (int s = 0; s < 4 * (w4 + 1); ++s)
                         u = mma_f32(sT[(16 * w4 + n) * LDC + 4 * s + g], sBeta[4 * s + g] * sR[(4 * s + g) * LDB + n], u);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) sU[(16 * w4 + 4 * g + e) * LDB + n] = u[e];
             } else {           // dU = (Ke dS, from the previous phase) + P^T dO (P^T upper triangular)
                 if constexpr (BF) {   // 32-token k-blocks 0, 1 (P^T's tiles below block w4 are zero)
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
                         du = mma_bf16x32(col8(sP + j0 * LDC + ci, LDC), col8(sDO + j0 * LDB + n, LDB), du);
@@ -970,14 +970,14 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     for (int s = 4 * w4; s < NKC; ++s)
                         du = mma_f32(sP[(4 * s + g) * LDC + 16 * w4 + n], sDO[(4 * s + g) * LDB + n], du);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) sDU[(16 * w4 + 4 * g + e) * LDB + n] = du[e];
             }
             __syncthreads();
             f32x4 dut = {0.f, 0.f, 0.f, 0.f};
             if (half == 0) {   // dU~ = T^T dU (T^T upper triangular); dv = diag(beta) dU~; dbeta += dU~ . R
                 if constexpr (BF) {   // 32-token k-blocks 0, 1 (T^T's tiles below block w4 are zero)
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         const int j0 = 32 * s + 8 * g, ci = 16 * w4 + n;
                         dut = mma_bf16x32(col8(sT + j0 * LDC + ci, LDC), col8(sDU + j0 * LDB + n, LDB), dut);
@@ -986,7 +986,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     for (int s = 4 * w4; s < NKC; ++s)
                         dut = mma_f32(sT[(4 * s + g) * LDC + 16 * w4 + n], sDU[(4 * s + g) * LDB + n], dut);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {   // dU~ replaces R in LDS (each element by the lane that read it)
                     const int i = 16 * w4 + 4 * g + e;
                     if (i < nvalid) dvp[rowi(i) * DV + col0 + n] = from_f32<E>(sBeta[i] * dut[e]);
@@ -995,13 +995,13 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 }
             } else {           // dP += dO U^T (all column tiles; those above the diagonal are discarded)
                 const bf16x4 ao = to_bf16x4(ld4s(sDO + (16 * w4 + n) * LDB + 4 * g));
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     {
                         if constexpr (BF) {
                             dMP[j] = mma_bf16(ao, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
                         } else {
-    #pragma unroll
+#pragma unroll
                             for (int s = 0; s < NB / 4; ++s)
                                 dMP[j] = mma_f32(sDO[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
                                                  dMP[j]);
@@ -1012,13 +1012,13 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
             __syncthreads();
             if (half == 0) {   // dM -= dU~ U^T (all column tiles; those above the diagonal are discarded)
                 const bf16x4 am = to_bf16x4(-ld4s(sR + (16 * w4 + n) * LDB + 4 * g));
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     {
                         if constexpr (BF) {
                             dMP[j] = mma_bf16(am, to_bf16x4(ld4s(sU + (16 * j + n) * LDB + 4 * g)), dMP[j]);
                         } else {
-    #pragma unroll
+#pragma unroll
                             for (int s = 0; s < NB / 4; ++s)
                                 dMP[j] = mma_f32(-sR[(16 * w4 + n) * LDB + 4 * s + g], sU[(16 * j + n) * LDB + 4 * s + g],
                                                  dMP[j]);
@@ -1032,7 +1032,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                 const bf16x4 ao = to_bf16x4(ld4s(sDO + ra));
                 const bf16x4 ar = to_bf16x4(-sBeta[16 * w4 + n] * ld4s(sR + ra));
                 const bf16x4 au = to_bf16x4(ld4s(sU + ra));
-    #pragma unroll
+#pragma unroll
                 for (int c2 = 0; c2 < NTH2; ++c2) {
                     const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * g;
                     const bf16x4 b0 = to_bf16x4(ld4s(sS0 + si)), b1 = to_bf16x4(ld4s(sDS + si));
@@ -1041,12 +1041,12 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
                     aE[c2] = mma_bf16(au, b1, aE[c2]);
                 }
             } else
-    #pragma unroll
+#pragma unroll
             for (int s = 0; s < NB / 4; ++s) {
                 const float ao = sDO[(16 * w4 + n) * LDB + 4 * s + g];
                 const float ar = -sBeta[16 * w4 + n] * sR[(16 * w4 + n) * LDB + 4 * s + g];
                 const float au = sU[(16 * w4 + n) * LDB + 4 * s + g];
-    #pragma unroll
+#pragma unroll
                 for (int c2 = 0; c2 < NTH2; ++c2) {
                     const int si = (16 * (ct0 + c2) + n) * LDSB + 4 * s + g;
                     const float b0 = sS0[si], b1 = sDS[si];
