@@ -130,3 +130,16 @@ def test_pipelined_vs_oracle(io):
             eo = np.linalg.norm(go[b, :, h] - r_out[b, :, h]) / np.linalg.norm(r_out[b, :, h])
             es = np.linalg.norm(gs[b, h] - r_st[b, h]) / np.linalg.norm(r_st[b, h])
             assert eo <= TOL[io] and es <= TOL[io], (b, h, eo, es)
+
+
+def test_pipelined_long_prefill_equals_prefill():
+    """The benchmark's long workload (65,536 tokens x 32 heads, bf16 d=128)
+    through the default 256-chunk ranges: bit-identical to the two calls on
+    the whole sequence, which the long oracle tests check on sampled heads."""
+    from kda_inputs import workload
+    inp = workload(2)
+    d = kda.to_device(inp)
+    note("[pipelined] long workload 1 x 65536 x 32 x 128 bf16, ranges of 256 chunks")
+    r_out, r_st = _reference(d, inp.log_alpha_min, None)
+    out, st = _pipelined(d, inp.log_alpha_min, None)
+    assert torch.equal(out, r_out) and torch.equal(st, r_st)
