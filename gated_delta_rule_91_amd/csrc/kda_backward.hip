@@ -25,14 +25,15 @@
 // Kernels, in order (the first two are the forward path's own):
 //   1. kda_prepare_kernel     forward update cards
 //   2. kda_scan_kernel        forward hand-off, also storing the state that
-//                             enters every chunk and the final one (and out,
-//                             for dg)
+//                             enters every chunk, tiled (tiled_state_index),
+//                             and out, for dg
 //   3. kda_bwd_card_kernel    per chunk, in parallel: the operands of the
 //                             reverse hand-off -- Ke, Qt^T, -Wk^T, dO in MFMA
 //                             operand order and P^T dO in accumulator order
 //   4. kda_bwd_scan_kernel    the reverse hand-off dS <- G dS + Qt^T dO - Wk^T dU
 //                             over the chunks in reverse, one workgroup per
-//                             16-column slice; stores the dS leaving every chunk
+//                             16-column slice; stores the dS leaving every
+//                             chunk, tiled
 //   5. kda_bwd_grad_kernel    per chunk, in parallel (eight waves): every token
 //                             gradient from S0, dS and the chunk's inputs
 //                             (bf16 MFMA for most products with bf16 I/O,
@@ -355,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// 5. token gradients: one workgroup of eight waves per chunk-head, fp32
-// throughout (LDS and fp32 MFMA).  The value-side quantities (R, U, dO, dU)
+// 5. token gradients: one workgroup of eight waves per chunk-head, fp32 LDS
+// tiles of the chunk's k^, q^, e^gamma, P and T.  The value-side quantities (R, U, dO, dU)
 // go through in 16-column blocks; the products that contract over the value
 // columns accumulate in registers across the blocks.  Wave w works on token
 // tile w % 4; the two halves of the workgroup (w / 4) run independent
@@ -367,10 +368,11 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
 // LDS), and no global load sits under a branch, so loads stay in flight
 // across the phases.  With bf16 I/O the
 // Gram matrices, R, U, Ke dS + P^T dO, dU~, dM, dP and the three products
-// that contract over the value columns take bf16 operands (16x16x16 MFMA,
-// fp32 accumulation), the operand precision of the forward cards; the
-// products after the column loop stay on fp32 MFMA (dgamma takes their
-// differences), as does all of fp32 I/O.
+// that contract over the value columns take bf16 operands (16x16x32 and
+// 16x16x16 MFMA, fp32 accumulation), the operand precision of the forward
+// cards; at d_k = 128 the column loop reads them from bf16 copies laid out so
+// that each fragment is one LDS read.  The products after the column loop
+// stay on fp32 MFMA (dgamma takes their differences), as does all of fp32 I/O.
 constexpr int kGradThreads = 512;
 
 template <int DK>
