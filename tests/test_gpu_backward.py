@@ -210,3 +210,28 @@ def test_backward_after_prefill_equals_backward(B, T, H, d, io):
         torch.cuda.synchronize()
         for name in ref:
             assert torch.equal(got[name], ref[name]), name
+
+
+def test_prefill_for_backward_in_place_state_and_empty_sequence():
+    """state_out may be state_in (the workspace keeps the entering state for
+    the backward half); with no tokens the call only passes the state through."""
+    inp = make_inputs(2, 200, 3, 64, 64, io_dtype="bf16", seed=7791, alpha_min=0.9, logit_mu=-1.0,
+                      with_state0=True)
+    t = kda.to_device(inp)
+    note("[backward after prefill] B=2 T=200 H=3 d=64 bf16, state in place; T=0")
+    args = (t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["g"])
+    r_out, r_st = kda.prefill(*args, inp.log_alpha_min, state_in=t["state0"])
+    ref = kda.backward(*args, inp.log_alpha_min, state_in=t["state0"], d_out=torch.ones_like(t["g"]))
+    s = t["state0"].clone()
+    out, st, ws = kda.prefill_for_backward(*args, inp.log_alpha_min, state_in=s, state_out=s)
+    torch.cuda.synchronize()
+    assert st.data_ptr() == s.data_ptr()
+    assert torch.equal(out, r_out) and torch.equal(st, r_st)
+    got = kda.backward_after_prefill(*args, out, ws, inp.log_alpha_min, d_out=torch.ones_like(t["g"]))
+    torch.cuda.synchronize()
+    for name in ref:
+        assert torch.equal(got[name], ref[name]), name
+    empty = [x[:, :0].contiguous() for x in args]
+    out, st, _ = kda.prefill_for_backward(*empty, inp.log_alpha_min, state_in=t["state0"])
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and torch.equal(st, t["state0"])
