@@ -469,7 +469,7 @@ def main():
         bstep(); fstep()
         torch.cuda.synchronize()
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        reps = 3
+        reps = 10
         e0.record()
         for _ in range(reps):
             bstep()
