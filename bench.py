@@ -327,6 +327,50 @@ def main():
         result["decode"] = {"workload": Wd["name"], "us_per_step": per_step_ms * 1e3, "GBps": gbs,
                             "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": DEC_BYTES * N * H,
                             "tokens_per_s": N / (per_step_ms * 1e-3)}
+        # a serving loop at a small batch (the first 8 sequences): the steps
+        # launched one by one from the host, and the same steps captured once
+        # in a HIP graph and replayed (the library records kernel launches
+        # only); both from the same state must give the same bits
+        Ns = 8
+        small = {n: sm[n][:, :Ns].contiguous() for n in sm}
+        st_e, st_g = dd["state0"][:Ns].clone(), dd["state0"][:Ns].clone()
+        out_e = torch.empty((Td, Ns, H, D), dtype=torch.bfloat16, device=dev)
+        out_g = torch.empty_like(out_e)
+
+        def sloop(st, outs):
+            for t in range(Td):
+                kda.decode_step(small["q"][t], small["k"][t], small["v"][t], small["log_alpha"][t],
+                                small["beta"][t], small["g"][t], st, floor_d, out=outs[t])
+
+        sloop(st_e, out_e)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sloop(st_g, out_g)
+        st_e.copy_(dd["state0"][:Ns])
+        st_g.copy_(dd["state0"][:Ns])
+        sloop(st_e, out_e)
+        graph.replay()
+        torch.cuda.synchronize()
+        same_g = torch.equal(st_e, st_g) and torch.equal(out_e, out_g)
+        e0.record()
+        for _ in range(reps):
+            sloop(st_e, out_e)
+        e1.record()
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / (reps * Td)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / (reps * Td)
+        log(f"[bench] decode of {Ns} sequences: {eager_us:.1f} us/step launched from the host, "
+            f"{graph_us:.1f} us/step replayed from a graph (identical: {same_g})")
+        result["decode"]["small_batch_graph"] = {
+            "workload": f"kda-decode N{Ns} H{H} d{D} bf16 {Td} steps", "eager_us_per_step": eager_us,
+            "graph_us_per_step": graph_us, "identical": same_g}
+        del graph, small, st_e, st_g, out_e, out_g
         # achievable-bandwidth reference in the same job: a plain device copy
         x = torch.empty(1 << 29, dtype=torch.float32, device=dev)
         y = torch.empty_like(x)
