@@ -30,6 +30,11 @@
  *    path allocates, and apart from kda_prefill_noalloc's fixed scratch area
  *    the library keeps no mutable global state, so calls are reentrant and
  *    may run concurrently on different streams.
+ *  - A call puts nothing on its streams but kernel launches (and, for
+ *    kda_prefill_pipelined, event records and waits): no memset, copy,
+ *    allocation or synchronisation, so it can be captured into a HIP graph
+ *    and replayed.  kda_prefill_noalloc looks up its scratch address on its
+ *    first call on a device; make that first call outside a capture.
  *  - All checks are synchronous and happen before any launch.  Invalid
  *    arguments return an error and launch nothing.  A failed launch returns
  *    KDA_ERR_HIP.  No data-dependent checks are made.  A NaN log_alpha entry
