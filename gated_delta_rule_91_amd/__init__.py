@@ -392,6 +392,53 @@ def backward_after_prefill(q, k, v, log_alpha, beta, g, out, workspace, log_alph
     return r
 
 
+_PREFILL_FUNCTION = None
+
+
+def _prefill_function():
+    """The torch.autograd.Function over the split training pair, created on
+    first use (torch is imported lazily)."""
+    global _PREFILL_FUNCTION
+    if _PREFILL_FUNCTION is None:
+        torch = _torch()
+
+        class PrefillFunction(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, log_alpha, beta, g, state_in, log_alpha_min):
+                out, state, ws = prefill_for_backward(q, k, v, log_alpha, beta, g, log_alpha_min,
+                                                      state_in=state_in)
+                ctx.save_for_backward(q, k, v, log_alpha, beta, g, out)
+                ctx.workspace = ws
+                ctx.log_alpha_min = log_alpha_min
+                ctx.has_state_in = state_in is not None
+                ctx.set_materialize_grads(False)
+                return out, state
+
+            @staticmethod
+            def backward(ctx, d_out, d_state):
+                q, k, v, log_alpha, beta, g, out = ctx.saved_tensors
+                r = backward_after_prefill(
+                    q, k, v, log_alpha, beta, g, out, ctx.workspace, ctx.log_alpha_min,
+                    d_out=None if d_out is None else d_out.contiguous(),
+                    d_state=None if d_state is None else d_state.contiguous(),
+                    want_dstate=ctx.has_state_in and ctx.needs_input_grad[6])
+                return r["dq"], r["dk"], r["dv"], r["dlog_alpha"], r["dbeta"], r["dg"], r["dstate0"], None
+
+        _PREFILL_FUNCTION = PrefillFunction
+    return _PREFILL_FUNCTION
+
+
+def prefill_autograd(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None):
+    """Differentiable prefill for training: returns (out, final state) like
+    prefill(), and loss.backward() then fills the gradients of q, k, v,
+    log_alpha, beta, g and state_in.  The forward pass is
+    kda_prefill_for_backward, whose workspace (cards and chunk states) is held
+    until the backward pass, kda_backward_after_prefill; the state gradient is
+    taken only when state_in is given and needs one, and an output the loss
+    does not use contributes nothing."""
+    return _prefill_function().apply(q, k, v, log_alpha, beta, g, state_in, float(log_alpha_min))
+
+
 def varlen_workspace_size(p: KdaProblem, n_seq: int) -> int:
     n = lib().kda_varlen_workspace_size(ctypes.byref(p), n_seq)
     if n == 0 and n_seq > 0:

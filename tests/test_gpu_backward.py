@@ -235,3 +235,40 @@ def test_prefill_for_backward_in_place_state_and_empty_sequence():
     out, st, _ = kda.prefill_for_backward(*empty, inp.log_alpha_min, state_in=t["state0"])
     torch.cuda.synchronize()
     assert out.numel() == 0 and torch.equal(st, t["state0"])
+
+
+@pytest.mark.parametrize("B,T,H,d,io", [(2, 300, 3, 128, "bf16"), (1, 200, 2, 64, "f32")])
+def test_prefill_autograd_matches_backward(B, T, H, d, io):
+    """prefill_autograd under torch.autograd: the forward equals prefill, and
+    the gradients loss.backward() leaves equal kda_backward's bit for bit,
+    for a loss on both outputs (state_in a leaf that needs its gradient) and
+    for a loss on the output alone (no state_in, the final state unused, so
+    its gradient arrives as None)."""
+    inp = make_inputs(B, T, H, d, d, io_dtype=io, seed=7800 + T, alpha_min=0.9, logit_mu=-1.0, with_state0=True)
+    t = kda.to_device(inp)
+    names = ("q", "k", "v", "log_alpha", "beta", "g")
+    grad_of = {"q": "dq", "k": "dk", "v": "dv", "log_alpha": "dlog_alpha", "beta": "dbeta", "g": "dg"}
+    gen = torch.Generator(device=DEV).manual_seed(T + 1)
+    w_out = torch.randn(t["g"].shape, device=DEV, generator=gen)
+    w_st = torch.randn((B, H, d, d), device=DEV, generator=gen)
+    for with_state in (True, False):
+        note(f"[autograd] B={B} T={T} H={H} d={d} {io}, loss on {'out and state' if with_state else 'out'}")
+        leaves = {n: t[n].clone().requires_grad_() for n in names}
+        s0 = t["state0"].clone().requires_grad_() if with_state else None
+        out, st = kda.prefill_autograd(*(leaves[n] for n in names), inp.log_alpha_min, state_in=s0)
+        plain = tuple(t[n] for n in names)
+        state_ref = t["state0"] if with_state else None
+        r_out, r_st = kda.prefill(*plain, inp.log_alpha_min, state_in=state_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out.detach(), r_out) and torch.equal(st.detach(), r_st)
+        loss = (out.float() * w_out).sum()
+        if with_state:
+            loss = loss + (st * w_st).sum()
+        loss.backward()
+        ref = kda.backward(*plain, inp.log_alpha_min, state_in=state_ref, d_out=w_out.to(t["g"].dtype),
+                           d_state=w_st if with_state else None, want_dstate=with_state)
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(leaves[n].grad, ref[grad_of[n]]), (n, with_state)
+        if with_state:
+            assert torch.equal(s0.grad, ref["dstate0"])
