@@ -10,8 +10,10 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix):
     workspace_size, chunk_prepare, chunk_scan, chunk_scan_checkpoints, segment_summarize,
     segment_combine, decode_step, backward_workspace_size, backward,
     varlen_workspace_size, varlen_prepare, varlen_scan, prefill_for_backward,
-    backward_after_prefill, pipelined_workspace_size
-Conveniences built from them: prefill, segmented_prefill, varlen_prefill.
+    backward_after_prefill, pipelined_workspace_size, varlen_backward_workspace_size,
+    varlen_backward
+Conveniences built from them: prefill, segmented_prefill, varlen_prefill, and
+prefill_autograd (a torch.autograd.Function over the split training pair).
 prefill_pipelined calls kda_prefill_pipelined (chunk ranges, the next range's
 cards prepared on a second stream during the current range's scan);
 prefill_noalloc calls kda_prefill_noalloc, which needs no workspace.
@@ -35,7 +37,8 @@ EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_chu
            "kda_segment_combine", "kda_decode_step", "kda_backward_workspace_size", "kda_backward",
            "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan",
            "kda_prefill_for_backward", "kda_backward_after_prefill", "kda_pipelined_workspace_size",
-           "kda_prefill_pipelined", "kda_prefill_noalloc", "kda_status_string")
+           "kda_prefill_pipelined", "kda_prefill_noalloc", "kda_varlen_backward_workspace_size",
+           "kda_varlen_backward", "kda_status_string")
 # bytes of kda_prefill_noalloc's fixed per-GPU scratch area (KDA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -85,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.kda_pipelined_workspace_size.restype = SZ
         L.kda_prefill_pipelined.argtypes = [PP, P, P, P, P, P, P, P, P, P, I32, P, SZ, P, P]
         L.kda_prefill_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P]
+        L.kda_varlen_backward_workspace_size.argtypes = [PP, I64]
+        L.kda_varlen_backward_workspace_size.restype = SZ
+        L.kda_varlen_backward.argtypes = [PP, I64] + [P] * 17 + [P, SZ, P]
         for f in EXPORTS[1:-1]:
             if not f.endswith("workspace_size"):
                 getattr(L, f).restype = I32
@@ -498,6 +504,40 @@ def varlen_prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, cu_seqlens
     """Chunked prefill of a packed variable-length batch.  Returns (out, final states [n_seq, H, dk, dv])."""
     ws = varlen_prepare(q, k, v, log_alpha, beta, log_alpha_min, cu_seqlens, workspace=workspace, stream=stream)
     return varlen_scan(ws, g, log_alpha_min, cu_seqlens, state_in=state_in, stream=stream)
+
+
+def varlen_backward_workspace_size(p: KdaProblem, n_seq: int) -> int:
+    return lib().kda_varlen_backward_workspace_size(ctypes.byref(p), n_seq)
+
+
+def varlen_backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, cu_seqlens, state_in=None, d_out=None,
+                    d_state=None, want_dstate: bool = True, workspace=None, stream=None) -> dict:
+    """Gradients of a packed batch (kda_varlen_backward): the token arrays are
+    [1, T, H, d] as for varlen_prefill, state_in and d_state [n_seq, H, dk, dv].
+    Returns the dict of backward(), with dstate0 [n_seq, H, dk, dv]."""
+    torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
+    p = _problem_of(q, v, log_alpha_min)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    n_seq = _cu(cu_seqlens, q.device)
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_in", state_in, (n_seq, H, dk, dv), torch.float32, q.device)
+    _expect("d_out", d_out, (B, T, H, dv), q.dtype, q.device)
+    _expect("d_state", d_state, (n_seq, H, dk, dv), torch.float32, q.device)
+    nbytes = varlen_backward_workspace_size(p, n_seq)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device)
+    r = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+             dlog_alpha=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta))
+    r["dstate0"] = torch.empty((n_seq, H, dk, dv), dtype=torch.float32, device=q.device) if want_dstate else None
+    _check("kda_varlen_backward", lib().kda_varlen_backward(
+        ctypes.byref(p), n_seq, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g),
+        _ptr(state_in), _ptr(d_out), _ptr(d_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]),
+        _ptr(r["dlog_alpha"]), _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace),
+        workspace.numel(), _stream(stream, q.device)))
+    return r
 
 
 def prefill(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, workspace=None, stream=None):

@@ -99,25 +99,80 @@ struct BCard {
 };
 
 // Workspace of one backward call, in this order, each region 256-byte aligned.
+// A uniform batch keeps NC + 1 entering-state slots per (b, h) (the last one
+// unused).  A packed batch (varlen: B sequences over T tokens) starts with the
+// chunk offsets and the chunk -> sequence map, sizes every per-chunk region
+// for the most chunks B sequences can have (ceil(T / C) + B per head), and
+// indexes the entering states like the cards: one slot per chunk-head.
 struct BwdLayout {
-    size_t cards, bcards, out, states, dstates, total;
-    __host__ __device__ BwdLayout(bool bf16, int64_t B, int64_t T, int H, int dk) {
+    size_t offs, seqmap, cards, bcards, out, states, dstates, total;
+    __host__ __device__ BwdLayout(bool bf16, int64_t B, int64_t T, int H, int dk, bool varlen = false) {
         const int64_t NC = (T + kChunk - 1) / kChunk;
-        const size_t chunks = (size_t)B * H * NC;
+        const size_t chunks = varlen ? (size_t)(NC + B) * H : (size_t)B * H * NC;
+        const size_t tokens = varlen ? (size_t)T : (size_t)B * T;
         const size_t esz = bf16 ? 2 : 4;
         const size_t card = bf16 ? (dk == 128 ? Card<__bf16, 128>::BYTES : Card<__bf16, 64>::BYTES)
                                  : (dk == 128 ? Card<float, 128>::BYTES : Card<float, 64>::BYTES);
         const size_t bcard = bf16 ? (dk == 128 ? BCard<__bf16, 128>::BYTES : BCard<__bf16, 64>::BYTES)
                                   : (dk == 128 ? BCard<float, 128>::BYTES : BCard<float, 64>::BYTES);
-        cards = 0;
+        offs = 0;
+        seqmap = varlen ? up((size_t)(B + 1) * 8) : 0;
+        cards = varlen ? seqmap + up((size_t)(NC + B) * 4) : 0;
         bcards = cards + up(chunks * card);
         out = bcards + up(chunks * bcard);
-        states = out + up((size_t)B * T * H * dk * esz);
-        dstates = states + up((chunks + (size_t)B * H) * (size_t)dk * dk * 4);   // NC + 1 slots per (b, h)
+        states = out + up(tokens * H * dk * esz);
+        dstates = states + up((chunks + (varlen ? 0 : (size_t)B * H)) * (size_t)dk * dk * 4);
         total = dstates + up(chunks * (size_t)dk * dk * 4);
     }
     __host__ __device__ static size_t up(size_t x) { return (x + 255) / 256 * 256; }
 };
+
+// The chunk-head of a workgroup of the reverse-card and gradient kernels (one
+// per chunk-head, heads fastest): its (row, head), the chunk's index in its
+// sequence, its tokens inside the sequence, the row of its first token along
+// the token axis (times H, plus the head), and its slots in the per-chunk
+// regions.  A packed batch numbers chunks across all sequences (chunk_off,
+// chunk_seq); workgroups past the last chunk have nothing to do.
+struct BwdChunk {
+    bool live;
+    int h, c, nvalid;
+    int64_t b, bh;
+    size_t row0;    // token row of the chunk's first token, times H, plus h
+    size_t cidx;    // card, reverse card and state gradient slot
+    size_t sidx;    // entering-state slot
+};
+template <bool VL>
+__device__ __forceinline__ BwdChunk bwd_chunk(const BackwardArgs& a, int64_t wg) {
+    BwdChunk r;
+    const int H = a.H;
+    r.h = (int)(wg % H);
+    const int64_t rest = wg / H;
+    if constexpr (VL) {
+        r.live = rest < a.chunk_off[a.B];
+        if (!r.live) return r;
+        r.b = a.chunk_seq[rest];
+        r.c = (int)(rest - a.chunk_off[r.b]);
+        const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, 0, 0, r.b, r.h, H);
+        const int64_t t0 = (int64_t)r.c * kChunk;
+        r.nvalid = (int)(sp.len - t0 < kChunk ? sp.len - t0 : kChunk);
+        r.row0 = (size_t)(sp.tok0 + t0) * H + r.h;
+        r.cidx = (size_t)sp.card0 + r.c;
+        r.sidx = r.cidx;
+        r.bh = r.b * H + r.h;
+    } else {
+        r.live = true;
+        const int NC = a.NC;
+        r.c = (int)(rest % NC);
+        r.b = rest / NC;
+        r.bh = r.b * H + r.h;
+        const int64_t t0 = (int64_t)r.c * kChunk;
+        r.nvalid = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+        r.row0 = ((size_t)r.b * a.T + t0) * H + r.h;
+        r.cidx = (size_t)r.bh * NC + r.c;
+        r.sidx = (size_t)r.bh * (NC + 1) + r.c;
+    }
+    return r;
+}
 
 // one element of a lane fragment
 __device__ __forceinline__ float frag_elem(float v, int) { return v; }
@@ -146,7 +201,7 @@ __device__ __forceinline__ void for_each_frag(const char* src, int t, F f) {
 
 // ---------------------------------------------------------------------------
 // 3. operands of the reverse hand-off (one workgroup per chunk-head)
-template <typename E, int DK>
+template <typename E, int DK, bool VL>
 __global__ __launch_bounds__(kThreads) void kda_bwd_card_kernel(BackwardArgs a) {
     using M = MM<E>;
     using CL = Card<E, DK>;
@@ -162,19 +217,12 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_card_kernel(BackwardArgs a) 
 
     const int t = threadIdx.x, lane = t & 63, g = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int H = a.H, NC = a.NC;
-    const int64_t T = a.T;
-    const int64_t wg = blockIdx.x;
-    const int h = (int)(wg % H);
-    const int64_t rest = wg / H;
-    const int c = (int)(rest % NC);
-    const int64_t b = rest / NC;
-    const int64_t bh = b * H + h;
-    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK);
-    const char* card = a.ws + L.cards + ((size_t)bh * NC + c) * CL::BYTES;
-    char* bcard = a.ws + L.bcards + ((size_t)bh * NC + c) * BC::BYTES;
-    const int64_t tok0 = (int64_t)c * C;
-    const int nvalid = (int)(T - tok0 < C ? T - tok0 : C);
+    const BwdChunk ck = bwd_chunk<VL>(a, blockIdx.x);
+    if (!ck.live) return;
+    const int H = a.H, nvalid = ck.nvalid;
+    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK, VL);
+    const char* card = a.ws + L.cards + ck.cidx * CL::BYTES;
+    char* bcard = a.ws + L.bcards + ck.cidx * BC::BYTES;
 
     // Ke (from Ke^T) -> row-major -> fragment order
     for_each_frag<E, DK, C>(card + CL::KET, t, [&](int r, int k, float x) { sStage[k * LDD + r] = from_f32<E>(x); });
@@ -191,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_card_kernel(BackwardArgs a) 
     // P^T, and dO = d_out * sigmoid(g) transposed (zero on padded tokens)
     for_each_frag<E, C, C>(card + CL::P, t, [&](int r, int k, float x) { sPT[k * LDC + r] = from_f32<E>(x); });
     {
-        const size_t row0 = ((size_t)b * T + tok0) * H + h;
+        const size_t row0 = ck.row0;
         const E* dop = reinterpret_cast<const E*>(a.d_out);
         const E* gp = reinterpret_cast<const E*>(a.g);
         const E* dsrc = dop ? dop : gp;   // loaded unconditionally, zeroed after when d_out is absent
@@ -239,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_card_kernel(BackwardArgs a) 
 // 4. reverse hand-off: one workgroup per (batch row, head, 16-column slice),
 // chunks in reverse.  Wave w owns dU rows (tokens) 16w..16w+15 and dS rows
 // w*DK/4 .. (w+1)*DK/4 - 1; dS^T and dU^T cross waves through LDS.
-template <typename E, int DK>
+template <typename E, int DK, bool VL>
 __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) {
     using M = MM<E>;
     using BC = BCard<E, DK>;
@@ -253,7 +301,6 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
     __shared__ __attribute__((aligned(16))) E sU[16 * LDS_U];
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4, n = lane & 15;
-    const int NC = a.NC;
     const int64_t BH = a.B * (int64_t)a.H;
     const int64_t x = blockIdx.x;
     const int xcd = (int)(x % kXcds);
@@ -262,7 +309,18 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
     const int64_t bh = (slot / NT) * kXcds + xcd;
     if (bh >= BH) return;
     const int col0 = 16 * tile;
-    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK);
+    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK, VL);
+    // this chain's chunks and its first chunk's slot in the per-chunk regions
+    int NC;
+    size_t cbase;
+    if constexpr (VL) {
+        const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, 0, 0, bh / a.H, (int)(bh % a.H), a.H);
+        NC = sp.nc;
+        cbase = (size_t)sp.card0;
+    } else {
+        NC = a.NC;
+        cbase = (size_t)bh * NC;
+    }
 
     f32x4 dS[MTS];
 #pragma unroll
@@ -276,8 +334,8 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
     for (int mt = 0; mt < MTS; ++mt) st4(sS + n * LDS_S + (DK / 4) * w + 16 * mt + 4 * g, dS[mt]);
     __syncthreads();
 
-    const char* bcards = a.ws + L.bcards + (size_t)bh * NC * BC::BYTES;
-    float* dstates = reinterpret_cast<float*>(a.ws + L.dstates) + (size_t)bh * NC * DK * DV;
+    const char* bcards = a.ws + L.bcards + cbase * BC::BYTES;
+    float* dstates = reinterpret_cast<float*>(a.ws + L.dstates) + cbase * DK * DV;
     // one chunk's operands in registers: a two-slot ring loads chunk c - 1
     // while chunk c computes (loads are unconditional: past chunk 0 the ring
     // re-reads chunk 0)
@@ -403,7 +461,7 @@ struct GradLds {
     static_assert((size_t)C * LDK <= 2 * (size_t)C * LDC, "dgamma fits over P and T");
 };
 
-template <typename E, int DK>
+template <typename E, int DK, bool VL>
 __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardArgs a) {
     using LY = GradLds<DK>;
     constexpr int C = kChunk, NB = LY::NB, DV = DK, NTH = kGradThreads;
@@ -441,22 +499,16 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int w4 = w & 3, half = w >> 2;   // token tile; which half of the workgroup
     const int ct0 = half * NTH2;           // this wave's first channel tile
-    const int H = a.H, NC = a.NC;
-    const int64_t T = a.T;
-    const int64_t wg = blockIdx.x;
-    const int h = (int)(wg % H);
-    const int64_t rest = wg / H;
-    const int c = (int)(rest % NC);
-    const int64_t b = rest / NC;
-    const int64_t bh = b * H + h;
-    const int64_t tok0 = (int64_t)c * C;
-    const int nvalid = (int)(T - tok0 < C ? T - tok0 : C);
-    const size_t row0 = ((size_t)b * T + tok0) * H + h;
+    const BwdChunk ck = bwd_chunk<VL>(a, blockIdx.x);
+    if (!ck.live) return;
+    const int H = a.H;
+    const int nvalid = ck.nvalid;
+    const size_t row0 = ck.row0;
     // token row of chunk token i (padded tokens re-read the last valid row)
     auto rowi = [&](int i) { return row0 + (size_t)(i < nvalid ? i : nvalid - 1) * H; };
-    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK);
-    const float* S0 = reinterpret_cast<const float*>(a.ws + L.states) + ((size_t)bh * (NC + 1) + c) * DK * DV;
-    const float* dSo = reinterpret_cast<const float*>(a.ws + L.dstates) + ((size_t)bh * NC + c) * DK * DV;
+    const BwdLayout L(sizeof(E) == 2, a.B, a.T, a.H, DK, VL);
+    const float* S0 = reinterpret_cast<const float*>(a.ws + L.states) + ck.sidx * DK * DV;
+    const float* dSo = reinterpret_cast<const float*>(a.ws + L.dstates) + ck.cidx * DK * DV;
     const E* qp = reinterpret_cast<const E*>(a.q);
     const E* kp = reinterpret_cast<const E*>(a.k);
 
@@ -1245,39 +1297,47 @@ __global__ __launch_bounds__(kGradThreads, 1) void kda_bwd_grad_kernel(BackwardA
     }
 }
 
-template <typename E, int DK>
+template <typename E, int DK, bool VL>
 hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
     const int64_t BH = a.B * (int64_t)a.H;
     if (BH == 0) return hipSuccess;
-    const int64_t chunks = BH * a.NC;
+    // one workgroup per chunk-head; a packed batch launches as many as its
+    // sequences can have chunks, and those past the last chunk return
+    const int64_t chunks = VL ? ((a.T + kChunk - 1) / kChunk + a.B) * a.H : BH * a.NC;
     if (chunks > 0) {
-        hipLaunchKernelGGL((kda_bwd_card_kernel<E, DK>), dim3((unsigned)chunks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((kda_bwd_card_kernel<E, DK, VL>), dim3((unsigned)chunks), dim3(kThreads), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t groups = (BH + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((kda_bwd_scan_kernel<E, DK>), dim3((unsigned)(groups * kXcds * (DK / 16))), dim3(kThreads), 0, s,
-                       a);
+    hipLaunchKernelGGL((kda_bwd_scan_kernel<E, DK, VL>), dim3((unsigned)(groups * kXcds * (DK / 16))), dim3(kThreads),
+                       0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || chunks == 0) return e;
-    hipLaunchKernelGGL((kda_bwd_grad_kernel<E, DK>), dim3((unsigned)chunks), dim3(kGradThreads), 0, s, a);
+    hipLaunchKernelGGL((kda_bwd_grad_kernel<E, DK, VL>), dim3((unsigned)chunks), dim3(kGradThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk) {
-    return T == 0 ? 0 : BwdLayout(bf16, B, T, H, dk).total;
+size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk, bool varlen) {
+    return T == 0 ? 0 : BwdLayout(bf16, B, T, H, dk, varlen).total;
 }
 
 hipError_t launch_backward_forward(bool bf16, int dk, const BackwardArgs& a, void* out, float* state_out,
                                    hipStream_t s) {
-    if (a.NC == 0 || a.B == 0) return hipSuccess;
-    const BwdLayout L(bf16, a.B, a.T, a.H, dk);
+    const bool vl = a.cu_seqlens != nullptr;
+    if (a.B == 0 || (vl ? a.T == 0 : a.NC == 0)) return hipSuccess;
+    const BwdLayout L(bf16, a.B, a.T, a.H, dk, vl);
     PrepareArgs p = {};
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.beta = a.beta;
     p.ws = a.ws + L.cards;
     p.B = a.B; p.T = a.T; p.H = a.H; p.NC = a.NC; p.floor_ = a.floor_;
+    if (vl) {   // the plan kernel writes the chunk offsets and the chunk -> sequence map first
+        p.cu_seqlens = a.cu_seqlens;
+        p.chunk_off = reinterpret_cast<int64_t*>(a.ws + L.offs);
+        p.chunk_seq = reinterpret_cast<int32_t*>(a.ws + L.seqmap);
+    }
     hipError_t e = launch_prepare(bf16, dk, p, s);
     if (e != hipSuccess) return e;
     ScanArgs f = {};
@@ -1287,19 +1347,30 @@ hipError_t launch_backward_forward(bool bf16, int dk, const BackwardArgs& a, voi
     f.ckpt_every = 1;
     f.states_tiled = true;
     f.B = a.B; f.T = a.T; f.H = a.H; f.NC = a.NC;
+    if (vl) {
+        f.cu_seqlens = a.cu_seqlens;
+        f.chunk_off = p.chunk_off;
+    }
     return launch_scan(bf16, dk, false, f, s);
 }
 
 hipError_t launch_backward(bool bf16, int dk, const BackwardArgs& a, bool recompute, hipStream_t s) {
     BackwardArgs b = a;
+    const bool vl = a.cu_seqlens != nullptr;
+    const BwdLayout L(bf16, a.B, a.T, a.H, dk, vl);
     if (recompute) {   // forward cards, then the forward hand-off keeping every chunk's entering state
-        const BwdLayout L(bf16, a.B, a.T, a.H, dk);
         b.out = a.ws + L.out;
         const hipError_t e = launch_backward_forward(bf16, dk, b, a.ws + L.out, nullptr, s);
         if (e != hipSuccess) return e;
     }
-    if (bf16) return dk == 128 ? launch_backward_t<__bf16, 128>(b, s) : launch_backward_t<__bf16, 64>(b, s);
-    return dk == 128 ? launch_backward_t<float, 128>(b, s) : launch_backward_t<float, 64>(b, s);
+    if (vl) {
+        b.chunk_off = reinterpret_cast<const int64_t*>(a.ws + L.offs);
+        b.chunk_seq = reinterpret_cast<const int32_t*>(a.ws + L.seqmap);
+        if (bf16) return dk == 128 ? launch_backward_t<__bf16, 128, true>(b, s) : launch_backward_t<__bf16, 64, true>(b, s);
+        return dk == 128 ? launch_backward_t<float, 128, true>(b, s) : launch_backward_t<float, 64, true>(b, s);
+    }
+    if (bf16) return dk == 128 ? launch_backward_t<__bf16, 128, false>(b, s) : launch_backward_t<__bf16, 64, false>(b, s);
+    return dk == 128 ? launch_backward_t<float, 128, false>(b, s) : launch_backward_t<float, 64, false>(b, s);
 }
 
 }  // namespace kda

@@ -89,16 +89,22 @@ struct BackwardArgs {
     const void* out;         // the forward output [B,T,H,dv] io dtype (set by launch_backward when it
                              // recomputes the forward)
     char* ws;                // backward_workspace_bytes
-    int64_t B, T;
+    int64_t B, T;            // packed variable-length batches: B = sequences, T = packed tokens
     int H, NC;
     float floor_;
+    const int32_t* cu_seqlens;   // or null (uniform batch); else [B+1] token offsets
+    const int64_t* chunk_off;    // with cu_seqlens: [B+1] first chunk of each sequence (in the workspace)
+    const int32_t* chunk_seq;    // with cu_seqlens: the sequence of each chunk (in the workspace)
 };
 
 size_t card_bytes(bool bf16, int dk);
-size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk);
+// varlen: a packed batch of B sequences over T tokens (cu_seqlens), whose
+// workspace starts with the chunk offsets and chunk -> sequence map
+size_t backward_workspace_bytes(bool bf16, int64_t B, int64_t T, int H, int dk, bool varlen = false);
 // The forward part of the backward: cards and every chunk's entering state
 // into the backward workspace, the output to `out`, the final state to
-// state_out (or nowhere).
+// state_out (or nowhere).  With a.cu_seqlens set (a packed batch) both calls
+// take chunk_off and chunk_seq from the workspace themselves.
 hipError_t launch_backward_forward(bool bf16, int dk, const BackwardArgs& a, void* out, float* state_out,
                                    hipStream_t s);
 // The backward; recompute: run the forward part first (its output into the

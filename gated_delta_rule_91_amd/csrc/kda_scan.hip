@@ -152,7 +152,8 @@ constexpr int kPrefetchMulti = 1;
 // stores); 2 every ckpt_every chunks (a branch around the stores: the cheaper
 // choice when checkpoints are sparse); 3 the state entering every chunk in
 // the backward's tiled layout (one 16-byte store per lane and 16-row tile),
-// no final-state slot
+// no final-state slot; NC + 1 slots per (row, head), or for a packed batch
+// one slot per chunk-head, indexed like the cards
 template <typename E, int DK, int NTW, bool SUMMARY, int CKPT>
 __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     using M = MM<E>;
@@ -255,8 +256,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     auto step = [&](auto full, const O& cur, int c) {
         constexpr bool FULL = decltype(full)::value;
         asm volatile("" ::"v"(cur.pf));   // the prefetch retires with the slot
-        if constexpr (CKPT == 3) {   // the state entering chunk c, tiled
-            float* dst = a.states + ((size_t)bh * (NC + 1) + c) * DK * DK;
+        if constexpr (CKPT == 3) {   // the state entering chunk c, tiled (a packed batch: at the card's slot)
+            float* dst = a.states + (a.cu_seqlens ? (size_t)sp.card0 + c : (size_t)bh * (NC + 1) + c) * DK * DK;
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll

@@ -243,6 +243,34 @@ kda_status kda_backward_after_prefill(const kda_problem* p, const void* q, const
                                       float* dlog_alpha, float* dbeta, void* dg, float* d_state_in,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of scratch kda_varlen_backward needs for a packed batch of n_seq
+ * sequences over p->seqlen tokens (p->batch must be 1): the chunk offsets
+ * and chunk -> sequence map, then the regions of kda_backward's workspace
+ * sized for the most chunks n_seq sequences can have, ceil(seqlen / 64) +
+ * n_seq per head.  Returns 0 if p is invalid or unsupported, or if there are
+ * no sequences or no tokens. */
+size_t kda_varlen_backward_workspace_size(const kda_problem* p, int64_t n_seq);
+
+/* Gradients of a packed variable-length batch for training [zuoshipin.com/
+ * article/18261 §四: the kernels serve training throughput; devpress.csdn.net
+ * K3 article §十六: each sequence keeps its own state]: kda_backward for every
+ * sequence of kda_varlen_prepare + kda_varlen_scan at once, all sequences'
+ * chunks in one launch per kernel.  The gradients equal kda_backward's on each
+ * sequence alone, bit for bit.
+ *   cu_seqlens: as for kda_varlen_prepare (same validity rules; a sequence
+ *   whose range is empty passes its state gradient through; token rows that
+ *   no sequence covers, possible only with offsets outside the rules, are
+ *   not written).
+ *   q, k, v, log_alpha, beta, g, d_out and the token gradients dq, dk, dv,
+ *   dlog_alpha, dbeta, dg: the packed [1, T, H, d] arrays, as for kda_backward.
+ *   state_in, d_state, d_state_in: [n_seq, H, dk, dv] fp32, or NULL.
+ *   workspace: >= kda_varlen_backward_workspace_size(p, n_seq) bytes. */
+kda_status kda_varlen_backward(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens, const void* q,
+                               const void* k, const void* v, const float* log_alpha, const float* beta,
+                               const void* g, const float* state_in, const void* d_out, const float* d_state,
+                               void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta, void* dg,
+                               float* d_state_in, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes of kda_prefill_pipelined with ranges of range_chunks
  * chunks: the carried state (B*H*dk*dv fp32), then the update cards of one
  * range for every (row, head), twice when the sequence spans more than one

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -173,6 +173,45 @@ def test_varlen_workspace_and_argument_errors(L):
     assert scan(g=None) == 1
     assert scan(si=MISALIGNED) == 1
     assert scan(ns=0, cu=None) == 0
+
+
+def _vbwd(L, pr, ns, ws, **kw):
+    names = ["cu", "q", "k", "v", "la", "b", "g", "s0", "do", "ds", "dq", "dk", "dv", "dla", "db", "dg", "ds0", "w"]
+    vals = {n: FAKE for n in names}
+    vals.update(s0=None, ds=None)
+    vals.update(kw)
+    n = kw.get("n", ws)
+    return L.kda_varlen_backward(ctypes.byref(pr), ns, *[vals[x] for x in names], n, None)
+
+
+def test_varlen_backward_workspace_and_argument_errors(L):
+    p = _p(batch=1, seqlen=1000)
+    up = lambda x: (x + 255) // 256 * 256
+    # chunk offsets, the sequence of each of at most ceil(1000/64) + 10 = 26
+    # chunks, then per chunk-head (26 x 3): forward card, reverse card, the
+    # forward output, and two fp32 states (entering, gradient leaving)
+    c = (16 + 10) * 3
+    want = (up(11 * 8) + up(26 * 4) + up(c * 74240) + up(c * 82432) + up(1000 * 3 * 128 * 2)
+            + 2 * up(c * 128 * 128 * 4))
+    ws = L.kda_varlen_backward_workspace_size(ctypes.byref(p), 10)
+    assert ws == want
+    assert L.kda_varlen_backward_workspace_size(ctypes.byref(_p()), 10) == 0        # batch must be 1
+    assert L.kda_varlen_backward_workspace_size(ctypes.byref(p), 0) == 0
+    assert L.kda_varlen_backward_workspace_size(ctypes.byref(_p(batch=1, seqlen=0)), 3) == 0
+    assert _vbwd(L, p, 10, ws, cu=None) == 1
+    assert _vbwd(L, p, 10, ws, cu=FAKE + 2) == 1      # int32 offsets need 4-byte alignment
+    assert _vbwd(L, p, 10, ws, q=MISALIGNED) == 1
+    assert _vbwd(L, p, 10, ws, dla=None) == 1
+    assert _vbwd(L, p, 10, ws, s0=MISALIGNED) == 1
+    assert _vbwd(L, p, 10, ws, w=None) == 1
+    assert _vbwd(L, p, 10, ws, n=ws - 1) == 3
+    assert _vbwd(L, _p(batch=2, seqlen=1000), 10, ws) == 1
+    assert _vbwd(L, _p(batch=1, seqlen=1000, dk=96, dv=96), 10, ws) == 2
+    assert _vbwd(L, p, -1, ws) == 1
+    # nothing to do: no sequences, or no tokens and no state gradient wanted
+    none = {n: None for n in ["q", "k", "v", "la", "b", "g", "dq", "dk", "dv", "dla", "db", "dg", "w", "ds0"]}
+    assert _vbwd(L, p, 0, 0, cu=None, w=None, ds0=None) == 0
+    assert _vbwd(L, _p(batch=1, seqlen=0), 3, 0, **none) == 0
 
 
 @pytest.mark.skipif(_have_gpu(), reason="only meaningful where no HIP device exists")

@@ -162,3 +162,111 @@ def test_varlen_overlapping_offsets_stay_inside_the_workspace():
     assert torch.equal(st[0:1], st1) and torch.equal(st[2:3], st1)
     assert torch.equal(st[4:5], st64)   # the clamped copy: its first chunk only
     assert not st[1].any() and not st[3].any()   # empty sequences from a zero state
+
+
+GRADS = ("dq", "dk", "dv", "dg", "dlog_alpha", "dbeta")
+
+
+def _varlen_grads(lengths, H, d, io, seed):
+    inp, dev, cu, s0 = _packed(lengths, H, d, io, seed)
+    gen = torch.Generator(device="cuda").manual_seed(seed + 1)
+    dout = torch.randn(dev["g"].shape, device="cuda", generator=gen).to(dev["g"].dtype)
+    dst = torch.randn((len(lengths), H, d, d), device="cuda", generator=gen)
+    args = (dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["g"])
+    gr = kda.varlen_backward(*args, inp.log_alpha_min, torch.from_numpy(cu).cuda(), state_in=s0, d_out=dout,
+                             d_state=dst)
+    torch.cuda.synchronize()
+    return inp, dev, cu, s0, dout, dst, args, gr
+
+
+@pytest.mark.parametrize("io,d,lengths", [
+    ("bf16", 128, [0, 1, 63, 64, 65, 200, 130, 7]),
+    ("f32", 64, [5, 0, 130, 64, 1, 300]),
+    ("bf16", 64, [777, 2, 0]),
+])
+def test_varlen_backward_equals_per_sequence_backward(io, d, lengths):
+    """kda_varlen_backward: all sequences' chunks in one launch per kernel,
+    bit-identical to kda_backward on each sequence alone (its slice of the
+    packed arrays, its own state and state gradient); an empty sequence
+    passes its state gradient through."""
+    H = 3
+    note(f"[varlen backward] exact vs per-sequence backward, {io} d={d} lengths={lengths}")
+    inp, dev, cu, s0, dout, dst, args, gr = _varlen_grads(lengths, H, d, io, seed=41 + d)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda x: x[:, a:b].contiguous()
+        ref = kda.backward(*(sl(x) for x in args), inp.log_alpha_min, state_in=s0[s:s + 1].contiguous(),
+                           d_out=sl(dout), d_state=dst[s:s + 1].contiguous())
+        torch.cuda.synchronize()
+        for n in GRADS:
+            assert torch.equal(gr[n][:, a:b], ref[n]), (s, n)
+        assert torch.equal(gr["dstate0"][s:s + 1], ref["dstate0"]), s
+
+
+def test_varlen_backward_vs_oracle():
+    """The same call against the fp64 adjoint of the step recurrence, run on
+    every sequence of the packing alone and packed back.  The measure is the
+    relative L2 per (row, head) slice of each gradient as the call returns it
+    (the packed [1, T, H, d] arrays) and per (sequence, head) for the state
+    gradients; a slice of one or two tokens would measure single bf16
+    roundings, not the method."""
+    rng = np.random.default_rng(9)
+    lengths = [int(x) for x in rng.integers(0, 260, size=6)] + [0, 64, 1]
+    H, d = 2, 128
+    note(f"[varlen backward] oracle parity bf16 d={d} lengths={lengths}")
+    inp, dev, cu, s0, dout, dst, args, gr = _varlen_grads(lengths, H, d, "bf16", seed=83)
+    f = lambda x: to_f64(x, "bf16")
+    do64 = dout.float().cpu().numpy().astype(np.float64)
+    ds64, s064 = dst.cpu().numpy().astype(np.float64), s0.cpu().numpy().astype(np.float64)
+    packed = {n: np.zeros(gr[n].shape) for n in GRADS}
+    ds0 = gr["dstate0"].cpu().numpy()
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = (slice(None), slice(a, b))
+        ref = oracle.kda_grad(f(inp.q[sl]), f(inp.k[sl]), f(inp.v[sl]), inp.log_alpha[sl], inp.beta[sl],
+                              f(inp.g[sl]), inp.log_alpha_min, s064[s:s + 1], d_out=do64[sl], d_state=ds64[s:s + 1])
+        for n in GRADS:
+            packed[n][sl] = ref[n]
+        for h in range(H):
+            e = _rel(ds0[s, h], ref["dstate0"][0, h])
+            assert e <= TOL["bf16"], ("dstate0", s, h, e)
+    for n in GRADS:
+        got = gr[n].float().cpu().numpy()
+        for h in range(H):
+            e = _rel(got[:, :, h], packed[n][:, :, h])
+            note(f"  {n} head {h}: {e:.2e}")
+            assert e <= TOL["bf16"], (n, h, e)
+
+
+def test_varlen_backward_medium_packing_equals_per_sequence():
+    """A training-sized packing: 16,384 tokens x 16 heads at d = 128 bf16 in
+    sequences of 64..4,096 tokens, bit-identical to per-sequence backward."""
+    rng = np.random.default_rng(13)
+    lengths, left = [], 16384
+    while left > 0:
+        n = min(left, int(np.exp(rng.uniform(np.log(64), np.log(4096)))))
+        lengths.append(n)
+        left -= n
+    H, d = 16, 128
+    note(f"[varlen backward] {len(lengths)} sequences, {sum(lengths)} tokens x {H} heads bf16")
+    inp, dev, cu, s0, dout, dst, args, gr = _varlen_grads(lengths, H, d, "bf16", seed=97)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda x: x[:, a:b].contiguous()
+        ref = kda.backward(*(sl(x) for x in args), inp.log_alpha_min, state_in=s0[s:s + 1].contiguous(),
+                           d_out=sl(dout), d_state=dst[s:s + 1].contiguous())
+        torch.cuda.synchronize()
+        for n in GRADS:
+            assert torch.equal(gr[n][:, a:b], ref[n]), (s, n)
+        assert torch.equal(gr["dstate0"][s:s + 1], ref["dstate0"]), s
+
+
+def test_varlen_backward_no_tokens_passes_state_gradients_through():
+    H, d = 2, 64
+    note("[varlen backward] three empty sequences")
+    e = torch.empty(1, 0, H, d, device="cuda")
+    dst = torch.randn(3, H, d, d, device="cuda")
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    gr = kda.varlen_backward(e, e, e, e, torch.empty(1, 0, H, device="cuda"), e, -0.1, cu, d_state=dst)
+    torch.cuda.synchronize()
+    assert torch.equal(gr["dstate0"], dst)
