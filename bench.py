@@ -564,6 +564,49 @@ def main():
                               "grad_TFLOPs_over_whole_call": bwd_flop * th / (bms * 1e-3) / 1e12,
                               "after_prefill": {"prefill_for_backward_ms": kms, "ms": ams,
                                                 "ratio_to_forward": ams / fms, "identical_to_backward": same}}
+        # the same 16,384 tokens x 16 heads as one packed row of sequences with
+        # log-uniform lengths of 64..4,096 tokens (seeded), through
+        # kda_varlen_backward; its gradients must equal kda_backward's on each
+        # sequence alone (checked on the first and the last)
+        rngv = np.random.default_rng(23)
+        Tp, lens = Bb * Tb, []
+        while sum(lens) < Tp:
+            lens.append(min(Tp - sum(lens), int(np.exp(rngv.uniform(np.log(64), np.log(4096))))))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        pk = {n: db[n].reshape((1, Tp) + tuple(db[n].shape[2:])) for n in ("q", "k", "v", "log_alpha", "beta", "g")}
+        d_out_p = d_out.reshape(1, Tp, Hb, D)
+        d_state_p = torch.randn((len(lens), Hb, D, D), device=dev, generator=gen)
+        pvl = kda.problem(1, Tp, Hb, D, D, kda.KDA_BF16, floor_b)
+        wsv = torch.empty(kda.varlen_backward_workspace_size(pvl, len(lens)), dtype=torch.uint8, device=dev)
+
+        def vstep():
+            return kda.varlen_backward(pk["q"], pk["k"], pk["v"], pk["log_alpha"], pk["beta"], pk["g"], floor_b, cu,
+                                       d_out=d_out_p, d_state=d_state_p, workspace=wsv)
+
+        gv = vstep()
+        torch.cuda.synchronize()
+        same_v = True
+        for s in (0, len(lens) - 1):
+            a0, a1 = int(sum(lens[:s])), int(sum(lens[:s + 1]))
+            one = {n: pk[n][:, a0:a1].contiguous() for n in pk}
+            rv = kda.backward(one["q"], one["k"], one["v"], one["log_alpha"], one["beta"], one["g"], floor_b,
+                              d_out=d_out_p[:, a0:a1].contiguous(), d_state=d_state_p[s:s + 1].contiguous())
+            torch.cuda.synchronize()
+            same_v = same_v and all(torch.equal(gv[n][:, a0:a1], rv[n]) for n in rv if n != "dstate0") and \
+                torch.equal(gv["dstate0"][s:s + 1], rv["dstate0"])
+        e0.record()
+        for _ in range(reps):
+            vstep()
+        e1.record()
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / reps
+        log(f"[bench] packed backward of {len(lens)} sequences ({min(lens)}..{max(lens)} tokens): {vms:.3f} ms "
+            f"(identical to per-sequence backward: {same_v})")
+        result["backward"]["varlen"] = {
+            "workload": f"kda-varlen-backward {len(lens)} sequences, {Tp} packed tokens, H{Hb} d{D} bf16",
+            "ms": vms, "n_seq": len(lens), "min_len": min(lens), "max_len": max(lens),
+            "identical_to_per_sequence": same_v}
+        del pk, d_out_p, d_state_p, wsv, gv
         del db, wsb, d_out, d_state, fwd_out, ref, got
         torch.cuda.empty_cache()
 
