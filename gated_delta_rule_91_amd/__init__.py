@@ -11,7 +11,7 @@ Entry points (same names as the C ABI, minus the ``kda_`` prefix):
     segment_combine, decode_step, backward_workspace_size, backward,
     varlen_workspace_size, varlen_prepare, varlen_scan, prefill_for_backward,
     backward_after_prefill, pipelined_workspace_size, varlen_backward_workspace_size,
-    varlen_backward
+    varlen_backward, varlen_prefill_for_backward, varlen_backward_after_prefill
 Conveniences built from them: prefill, segmented_prefill, varlen_prefill, and
 prefill_autograd (a torch.autograd.Function over the split training pair).
 prefill_pipelined calls kda_prefill_pipelined (chunk ranges, the next range's
@@ -38,7 +38,8 @@ EXPORTS = ("kda_workspace_size", "kda_chunk_prepare", "kda_chunk_scan", "kda_chu
            "kda_varlen_workspace_size", "kda_varlen_prepare", "kda_varlen_scan",
            "kda_prefill_for_backward", "kda_backward_after_prefill", "kda_pipelined_workspace_size",
            "kda_prefill_pipelined", "kda_prefill_noalloc", "kda_varlen_backward_workspace_size",
-           "kda_varlen_backward", "kda_status_string")
+           "kda_varlen_backward", "kda_varlen_prefill_for_backward", "kda_varlen_backward_after_prefill",
+           "kda_status_string")
 # bytes of kda_prefill_noalloc's fixed per-GPU scratch area (KDA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.kda_varlen_backward_workspace_size.argtypes = [PP, I64]
         L.kda_varlen_backward_workspace_size.restype = SZ
         L.kda_varlen_backward.argtypes = [PP, I64] + [P] * 17 + [P, SZ, P]
+        L.kda_varlen_prefill_for_backward.argtypes = [PP, I64] + [P] * 10 + [P, SZ, P]
+        L.kda_varlen_backward_after_prefill.argtypes = [PP, I64] + [P] * 17 + [P, SZ, P]
         for f in EXPORTS[1:-1]:
             if not f.endswith("workspace_size"):
                 getattr(L, f).restype = I32
@@ -410,10 +413,15 @@ def _prefill_function():
 
         class PrefillFunction(torch.autograd.Function):
             @staticmethod
-            def forward(ctx, q, k, v, log_alpha, beta, g, state_in, log_alpha_min):
-                out, state, ws = prefill_for_backward(q, k, v, log_alpha, beta, g, log_alpha_min,
-                                                      state_in=state_in)
+            def forward(ctx, q, k, v, log_alpha, beta, g, state_in, log_alpha_min, cu_seqlens):
+                if cu_seqlens is None:
+                    out, state, ws = prefill_for_backward(q, k, v, log_alpha, beta, g, log_alpha_min,
+                                                          state_in=state_in)
+                else:
+                    out, state, ws = varlen_prefill_for_backward(q, k, v, log_alpha, beta, g, log_alpha_min,
+                                                                 cu_seqlens, state_in=state_in)
                 ctx.save_for_backward(q, k, v, log_alpha, beta, g, out)
+                ctx.cu_seqlens = cu_seqlens
                 ctx.workspace = ws
                 ctx.log_alpha_min = log_alpha_min
                 ctx.has_state_in = state_in is not None
@@ -423,26 +431,32 @@ def _prefill_function():
             @staticmethod
             def backward(ctx, d_out, d_state):
                 q, k, v, log_alpha, beta, g, out = ctx.saved_tensors
-                r = backward_after_prefill(
-                    q, k, v, log_alpha, beta, g, out, ctx.workspace, ctx.log_alpha_min,
-                    d_out=None if d_out is None else d_out.contiguous(),
-                    d_state=None if d_state is None else d_state.contiguous(),
-                    want_dstate=ctx.has_state_in and ctx.needs_input_grad[6])
-                return r["dq"], r["dk"], r["dv"], r["dlog_alpha"], r["dbeta"], r["dg"], r["dstate0"], None
+                kw = dict(d_out=None if d_out is None else d_out.contiguous(),
+                          d_state=None if d_state is None else d_state.contiguous(),
+                          want_dstate=ctx.has_state_in and ctx.needs_input_grad[6])
+                if ctx.cu_seqlens is None:
+                    r = backward_after_prefill(q, k, v, log_alpha, beta, g, out, ctx.workspace, ctx.log_alpha_min,
+                                               **kw)
+                else:
+                    r = varlen_backward_after_prefill(q, k, v, log_alpha, beta, g, out, ctx.workspace,
+                                                      ctx.log_alpha_min, ctx.cu_seqlens, **kw)
+                return r["dq"], r["dk"], r["dv"], r["dlog_alpha"], r["dbeta"], r["dg"], r["dstate0"], None, None
 
         _PREFILL_FUNCTION = PrefillFunction
     return _PREFILL_FUNCTION
 
 
-def prefill_autograd(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None):
+def prefill_autograd(q, k, v, log_alpha, beta, g, log_alpha_min: float, state_in=None, cu_seqlens=None):
     """Differentiable prefill for training: returns (out, final state) like
-    prefill(), and loss.backward() then fills the gradients of q, k, v,
+    prefill(), or like varlen_prefill() for a packed batch when cu_seqlens is
+    given, and loss.backward() then fills the gradients of q, k, v,
     log_alpha, beta, g and state_in.  The forward pass is
-    kda_prefill_for_backward, whose workspace (cards and chunk states) is held
-    until the backward pass, kda_backward_after_prefill; the state gradient is
-    taken only when state_in is given and needs one, and an output the loss
-    does not use contributes nothing."""
-    return _prefill_function().apply(q, k, v, log_alpha, beta, g, state_in, float(log_alpha_min))
+    kda_prefill_for_backward (kda_varlen_prefill_for_backward), whose
+    workspace (cards and chunk states) is held until the backward pass,
+    kda_backward_after_prefill (kda_varlen_backward_after_prefill); the state
+    gradient is taken only when state_in is given and needs one, and an
+    output the loss does not use contributes nothing."""
+    return _prefill_function().apply(q, k, v, log_alpha, beta, g, state_in, float(log_alpha_min), cu_seqlens)
 
 
 def varlen_workspace_size(p: KdaProblem, n_seq: int) -> int:
@@ -537,6 +551,61 @@ def varlen_backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, cu_seqlen
         _ptr(state_in), _ptr(d_out), _ptr(d_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]),
         _ptr(r["dlog_alpha"]), _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace),
         workspace.numel(), _stream(stream, q.device)))
+    return r
+
+
+def varlen_prefill_for_backward(q, k, v, log_alpha, beta, g, log_alpha_min: float, cu_seqlens, state_in=None,
+                                out=None, state_out=None, want_state: bool = True, workspace=None, stream=None):
+    """varlen_prefill whose cards and chunk states stay in a varlen backward
+    workspace (kda_varlen_prefill_for_backward).  Returns (out, state_out,
+    workspace); pass out and workspace to varlen_backward_after_prefill."""
+    torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    n_seq = _cu(cu_seqlens, q.device)
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_in", state_in, (n_seq, H, dk, dv), torch.float32, q.device)
+    _expect("out", out, (B, T, H, dv), q.dtype, q.device)
+    _expect("state_out", state_out, (n_seq, H, dk, dv), torch.float32, q.device)
+    p = _problem_of(q, v, log_alpha_min)
+    nbytes = varlen_backward_workspace_size(p, n_seq)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _expect_workspace(workspace, q.device)
+    if out is None:
+        out = torch.empty_like(g)
+    if state_out is None and want_state:
+        state_out = torch.empty((n_seq, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check("kda_varlen_prefill_for_backward", lib().kda_varlen_prefill_for_backward(
+        ctypes.byref(p), n_seq, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g),
+        _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), workspace.numel(), _stream(stream, q.device)))
+    return out, state_out, workspace
+
+
+def varlen_backward_after_prefill(q, k, v, log_alpha, beta, g, out, workspace, log_alpha_min: float, cu_seqlens,
+                                  d_out=None, d_state=None, want_dstate: bool = True, stream=None) -> dict:
+    """varlen_backward without its forward pass: out and workspace come from
+    varlen_prefill_for_backward on the same inputs.  Returns the same dict."""
+    torch = _torch()
+    _expect_prefill_inputs(q, k, v, log_alpha, beta)
+    p = _problem_of(q, v, log_alpha_min)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    n_seq = _cu(cu_seqlens, q.device)
+    _expect("g", g, (B, T, H, dv), q.dtype, q.device)
+    _expect("out", out, (B, T, H, dv), q.dtype, q.device)
+    _expect("d_out", d_out, (B, T, H, dv), q.dtype, q.device)
+    _expect("d_state", d_state, (n_seq, H, dk, dv), torch.float32, q.device)
+    _expect_workspace(workspace, q.device)
+    r = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+             dlog_alpha=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta))
+    r["dstate0"] = torch.empty((n_seq, H, dk, dv), dtype=torch.float32, device=q.device) if want_dstate else None
+    _check("kda_varlen_backward_after_prefill", lib().kda_varlen_backward_after_prefill(
+        ctypes.byref(p), n_seq, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(g),
+        _ptr(out), _ptr(d_out), _ptr(d_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dlog_alpha"]),
+        _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dstate0"]), _ptr(workspace), workspace.numel(),
+        _stream(stream, q.device)))
     return r
 
 

@@ -465,6 +465,65 @@ kda_status kda_varlen_backward(const kda_problem* p, int64_t n_seq, const int32_
     return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, true, (hipStream_t)stream));
 }
 
+kda_status kda_varlen_prefill_for_backward(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
+                                           const void* q, const void* k, const void* v, const float* log_alpha,
+                                           const float* beta, const void* g, const float* state_in, void* out,
+                                           float* state_out, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+    kda_status st = check_varlen(p, n_seq);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->seqlen > 0;
+    if (!ok_beta(cu_seqlens, n_seq > 0) || !ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) ||
+        !ok_ptr(log_alpha, tokens) || !ok_beta(beta, tokens) || !ok_ptr(g, tokens) || !ok_ptr(out, tokens) ||
+        !ok_ptr(workspace, tokens && n_seq > 0) || !ok_opt_ptr(state_in) || !ok_opt_ptr(state_out))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_varlen_backward_workspace_size(p, n_seq)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (n_seq == 0 || (!tokens && !state_out)) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!tokens) {   // every sequence empty: its state passes through
+        kda_problem each = *p;
+        each.batch = n_seq;
+        return copy_state(&each, state_in, state_out, s);
+    }
+    BackwardArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.g = g; a.state_in = state_in;
+    a.ws = static_cast<char*>(workspace);
+    a.cu_seqlens = cu_seqlens;
+    a.B = n_seq; a.T = p->seqlen; a.H = p->heads; a.NC = 0; a.floor_ = p->log_alpha_min;
+    return hip_status(launch_backward_forward(p->io_dtype == KDA_BF16, p->dk, a, out, state_out, s));
+}
+
+kda_status kda_varlen_backward_after_prefill(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
+                                             const void* q, const void* k, const void* v, const float* log_alpha,
+                                             const float* beta, const void* g, const void* out, const void* d_out,
+                                             const float* d_state, void* dq, void* dk, void* dv, float* dlog_alpha,
+                                             float* dbeta, void* dg, float* d_state_in, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+    kda_status st = check_varlen(p, n_seq);
+    if (st != KDA_OK) return st;
+    const bool tokens = p->seqlen > 0;
+    if (!ok_beta(cu_seqlens, n_seq > 0) || !ok_ptr(q, tokens) || !ok_ptr(k, tokens) || !ok_ptr(v, tokens) ||
+        !ok_ptr(log_alpha, tokens) || !ok_beta(beta, tokens) || !ok_ptr(g, tokens) || !ok_ptr(out, tokens) ||
+        !ok_ptr(dq, tokens) || !ok_ptr(dk, tokens) || !ok_ptr(dv, tokens) || !ok_ptr(dlog_alpha, tokens) ||
+        !ok_beta(dbeta, tokens) || !ok_ptr(dg, tokens) || !ok_ptr(workspace, tokens && n_seq > 0) ||
+        !ok_opt_ptr(d_out) || !ok_opt_ptr(d_state) || !ok_opt_ptr(d_state_in))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < kda_varlen_backward_workspace_size(p, n_seq)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (n_seq == 0 || (!tokens && !d_state_in)) return KDA_OK;
+    if ((st = device_ready()) != KDA_OK) return st;
+    BackwardArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.g = g;
+    a.d_out = d_out; a.d_state = d_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dg = dg;
+    a.d_state_in = d_state_in;
+    a.out = out;
+    a.ws = static_cast<char*>(workspace);
+    a.B = n_seq; a.T = p->seqlen; a.H = p->heads; a.NC = 0; a.floor_ = p->log_alpha_min;
+    if (tokens) a.cu_seqlens = cu_seqlens;   // else the uniform path passes the state gradients through
+    return hip_status(launch_backward(p->io_dtype == KDA_BF16, p->dk, a, false, (hipStream_t)stream));
+}
+
 size_t kda_pipelined_workspace_size(const kda_problem* p, int32_t range_chunks) {
     if (check_problem(p) != KDA_OK || range_chunks < 1) return 0;
     const int64_t rc = range_of(p, range_chunks);

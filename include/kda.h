@@ -271,6 +271,26 @@ kda_status kda_varlen_backward(const kda_problem* p, int64_t n_seq, const int32_
                                void* dq, void* dk, void* dv, float* dlog_alpha, float* dbeta, void* dg,
                                float* d_state_in, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The split training pair for a packed batch [the same passages]: a
+ * kda_varlen_prepare + kda_varlen_scan whose cards and chunk states stay in a
+ * kda_varlen_backward workspace, then the backward without its own forward
+ * pass.  Arguments as for kda_varlen_backward, plus out and state_out as for
+ * kda_varlen_scan; kda_varlen_backward_after_prefill takes the same problem,
+ * cu_seqlens, inputs and workspace, and `out` as the first call left it, and
+ * gives kda_varlen_backward's gradients bit for bit (inputs that differ from
+ * the first call's give gradients of the wrong point; this is not checked). */
+kda_status kda_varlen_prefill_for_backward(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
+                                           const void* q, const void* k, const void* v, const float* log_alpha,
+                                           const float* beta, const void* g, const float* state_in, void* out,
+                                           float* state_out, void* workspace, size_t workspace_bytes,
+                                           void* stream);
+kda_status kda_varlen_backward_after_prefill(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
+                                             const void* q, const void* k, const void* v, const float* log_alpha,
+                                             const float* beta, const void* g, const void* out, const void* d_out,
+                                             const float* d_state, void* dq, void* dk, void* dv, float* dlog_alpha,
+                                             float* dbeta, void* dg, float* d_state_in, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
 /* Workspace bytes of kda_prefill_pipelined with ranges of range_chunks
  * chunks: the carried state (B*H*dk*dv fp32), then the update cards of one
  * range for every (row, head), twice when the sequence spans more than one

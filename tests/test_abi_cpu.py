@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     assert sorted(kda.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -212,6 +212,34 @@ def test_varlen_backward_workspace_and_argument_errors(L):
     none = {n: None for n in ["q", "k", "v", "la", "b", "g", "dq", "dk", "dv", "dla", "db", "dg", "w", "ds0"]}
     assert _vbwd(L, p, 0, 0, cu=None, w=None, ds0=None) == 0
     assert _vbwd(L, _p(batch=1, seqlen=0), 3, 0, **none) == 0
+
+
+def test_varlen_split_pair_argument_errors(L):
+    p = _p(batch=1, seqlen=1000)
+    ws = L.kda_varlen_backward_workspace_size(ctypes.byref(p), 10)
+    fwd = lambda pr=p, ns=10, cu=FAKE, q=FAKE, o=FAKE, w=FAKE, n=ws, so=None: L.kda_varlen_prefill_for_backward(
+        ctypes.byref(pr), ns, cu, q, FAKE, FAKE, FAKE, FAKE, FAKE, None, o, so, w, n, None)
+    assert fwd(cu=None) == 1
+    assert fwd(q=None) == 1
+    assert fwd(o=None) == 1
+    assert fwd(w=None) == 1
+    assert fwd(n=ws - 1) == 3
+    assert fwd(pr=_p(batch=2, seqlen=1000)) == 1
+    assert fwd(ns=0, cu=None, w=None, n=0) == 0
+    assert fwd(pr=_p(batch=1, seqlen=0), q=None, o=None, w=None, n=0) == 0    # no tokens, no state_out
+    names = ["cu", "q", "k", "v", "la", "b", "g", "o", "do", "ds", "dq", "dk", "dv", "dla", "db", "dg", "ds0", "w"]
+
+    def bwd(pr=p, ns=10, n=ws, **kw):
+        vals = {x: FAKE for x in names}
+        vals.update(ds=None, ds0=None)
+        vals.update(kw)
+        return L.kda_varlen_backward_after_prefill(ctypes.byref(pr), ns, *[vals[x] for x in names], n, None)
+
+    assert bwd(cu=None) == 1
+    assert bwd(o=None) == 1
+    assert bwd(dq=MISALIGNED) == 1
+    assert bwd(n=ws - 1) == 3
+    assert bwd(ns=0, cu=None, w=None, n=0) == 0
 
 
 @pytest.mark.skipif(_have_gpu(), reason="only meaningful where no HIP device exists")

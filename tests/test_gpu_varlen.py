@@ -270,3 +270,33 @@ def test_varlen_backward_no_tokens_passes_state_gradients_through():
     gr = kda.varlen_backward(e, e, e, e, torch.empty(1, 0, H, device="cuda"), e, -0.1, cu, d_state=dst)
     torch.cuda.synchronize()
     assert torch.equal(gr["dstate0"], dst)
+
+
+@pytest.mark.parametrize("io,d,lengths", [("bf16", 128, [0, 1, 63, 64, 65, 200, 130, 7]), ("f32", 64, [300, 5, 0, 64])])
+def test_varlen_split_pair_and_autograd_equal_varlen_backward(io, d, lengths):
+    """kda_varlen_prefill_for_backward + kda_varlen_backward_after_prefill, and
+    prefill_autograd with cu_seqlens under loss.backward(), give what
+    varlen_prefill and kda_varlen_backward give, bit for bit."""
+    H = 3
+    note(f"[varlen split pair] {io} d={d} lengths={lengths}")
+    inp, dev, cu, s0, dout, dst, args, ref = _varlen_grads(lengths, H, d, io, seed=61 + d)
+    cu_t = torch.from_numpy(cu).cuda()
+    r_out, r_st = kda.varlen_prefill(*args, inp.log_alpha_min, cu_t, state_in=s0)
+    out, st, ws = kda.varlen_prefill_for_backward(*args, inp.log_alpha_min, cu_t, state_in=s0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, r_out) and torch.equal(st, r_st)
+    got = kda.varlen_backward_after_prefill(*args, out, ws, inp.log_alpha_min, cu_t, d_out=dout, d_state=dst)
+    torch.cuda.synchronize()
+    for n in ref:
+        assert torch.equal(got[n], ref[n]), n
+    names = ("q", "k", "v", "log_alpha", "beta", "g")
+    leaves = [x.clone().requires_grad_() for x in args]
+    s0l = s0.clone().requires_grad_()
+    o, s = kda.prefill_autograd(*leaves, inp.log_alpha_min, state_in=s0l, cu_seqlens=cu_t)
+    ((o.float() * dout.float()).sum() + (s * dst).sum()).backward()
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), r_out) and torch.equal(s.detach(), r_st)
+    grad_of = {"q": "dq", "k": "dk", "v": "dv", "log_alpha": "dlog_alpha", "beta": "dbeta", "g": "dg"}
+    for n, x in zip(names, leaves):
+        assert torch.equal(x.grad, ref[grad_of[n]]), n
+    assert torch.equal(s0l.grad, ref["dstate0"])
