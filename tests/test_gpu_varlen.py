@@ -300,3 +300,33 @@ def test_varlen_split_pair_and_autograd_equal_varlen_backward(io, d, lengths):
     for n, x in zip(names, leaves):
         assert torch.equal(x.grad, ref[grad_of[n]]), n
     assert torch.equal(s0l.grad, ref["dstate0"])
+
+
+def test_varlen_backward_overlapping_offsets_stay_inside_the_workspace():
+    """The backward over offsets that go back (as in the forward test above:
+    12 chunks for a workspace that holds 9): every kernel takes the clamped
+    chunk offsets, so no access leaves the arrays or the workspace.  The
+    complete copies (sequences 0 and 2, the same state seed) write identical
+    values, so token rows past the first chunk equal an ordinary backward;
+    each sequence's state gradient is its own."""
+    H, d, T = 2, 128, 256
+    note("[varlen backward] overlapping offsets, 12 chunks for a 9-chunk workspace")
+    inp = make_inputs(1, T, H, d, d, io_dtype="bf16", seed=48, alpha_min=0.9, logit_mu=-1.0)
+    dev = kda.to_device(inp)
+    args = tuple(dev[n] for n in ("q", "k", "v", "log_alpha", "beta", "g"))
+    cu = torch.tensor([0, 256, 0, 256, 0, 256], dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    dout = torch.randn(dev["g"].shape, device="cuda", generator=gen).to(torch.bfloat16)
+    dst = torch.randn((5, H, d, d), device="cuda", generator=gen)
+    dst[2] = dst[0]
+    gr = kda.varlen_backward(*args, inp.log_alpha_min, cu, d_out=dout, d_state=dst)
+    full = kda.backward(*args, inp.log_alpha_min, d_out=dout, d_state=dst[0:1].contiguous())
+    first = lambda x: x[:, :64].contiguous()
+    one = kda.backward(*(first(x) for x in args), inp.log_alpha_min, d_out=first(dout),
+                       d_state=dst[4:5].contiguous())
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(gr[n][:, 64:], full[n][:, 64:]), n
+    assert torch.equal(gr["dstate0"][0:1], full["dstate0"]) and torch.equal(gr["dstate0"][2:3], full["dstate0"])
+    assert torch.equal(gr["dstate0"][4:5], one["dstate0"])   # the clamped copy: its first chunk only
+    assert torch.equal(gr["dstate0"][1], dst[1]) and torch.equal(gr["dstate0"][3], dst[3])   # empty sequences
