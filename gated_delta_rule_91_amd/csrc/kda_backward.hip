@@ -150,9 +150,13 @@ __device__ __forceinline__ BwdChunk bwd_chunk(const BackwardArgs& a, int64_t wg)
     if constexpr (VL) {
         r.live = rest < a.chunk_off[a.B];
         if (!r.live) return r;
-        r.b = a.chunk_seq[rest];
-        r.c = (int)(rest - a.chunk_off[r.b]);
-        const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, 0, 0, r.b, r.h, H);
+        const int32_t sq = a.chunk_seq[rest];
+        r.b = sq < 0 ? 0 : (sq >= a.B ? a.B - 1 : sq);
+        const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, 0, 0, a.B, r.b, r.h, H);
+        const int64_t cc = rest - sp.chunk0;
+        r.live = cc >= 0 && cc < sp.nc;   // a chunk outside its sequence's (clamped) span has nothing to do
+        if (!r.live) return r;
+        r.c = (int)cc;
         const int64_t t0 = (int64_t)r.c * kChunk;
         r.nvalid = (int)(sp.len - t0 < kChunk ? sp.len - t0 : kChunk);
         r.row0 = (size_t)(sp.tok0 + t0) * H + r.h;
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_scan_kernel(BackwardArgs a) 
     int NC;
     size_t cbase;
     if constexpr (VL) {
-        const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, 0, 0, bh / a.H, (int)(bh % a.H), a.H);
+        const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, 0, 0, a.B, bh / a.H, (int)(bh % a.H), a.H);
         NC = sp.nc;
         cbase = (size_t)sp.card0;
     } else {

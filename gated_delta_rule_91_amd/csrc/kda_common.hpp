@@ -155,30 +155,49 @@ struct Card {
 //    send an access outside the arrays); its NC_s chunks' cards start at
 //    card chunk_off[s]*H + h*NC_s, chunk_off being the prefix sum of NC_s.
 struct SeqSpan {
-    int64_t tok0;    // first token (row index along the packed token axis)
-    int64_t len;     // tokens
-    int nc;          // chunks
-    int64_t card0;   // card index of chunk 0 of (sequence, head)
+    int64_t tok0;     // first token (row index along the packed token axis)
+    int64_t len;      // tokens
+    int nc;           // chunks
+    int64_t chunk0;   // packed batch: global index of the sequence's first chunk (0 for a uniform batch)
+    int64_t card0;    // card index of chunk 0 of (sequence, head)
 };
 __device__ __forceinline__ void seq_bounds(const int32_t* cu, int64_t s, int64_t T, int64_t& st, int64_t& en) {
     const int64_t a = cu[s], b = cu[s + 1];
     st = a < 0 ? 0 : (a > T ? T : a);
     en = b < st ? st : (b > T ? T : b);
 }
+// nseq: sequences of a packed batch.  CLAMP: the chunk offsets were read
+// back from a workspace an earlier call filled, so they are clamped to the
+// chunks the workspace holds (ceil(T/C) + nseq) and to the sequence's own
+// chunk count: whatever the workspace or cu_seqlens hold, no access leaves
+// the workspace or the token arrays (offsets the plan kernel wrote for these
+// cu_seqlens pass unchanged).  The prepare, which runs right after the plan
+// kernel in the same call, takes them as they are.
+template <bool CLAMP = true>
 __device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, const int64_t* chunk_off, int64_t T, int64_t rs,
-                                            int NC, int64_t b, int h, int H) {
+                                            int NC, int64_t nseq, int64_t b, int h, int H) {
     SeqSpan r;
     if (cu) {
         int64_t st, en;
         seq_bounds(cu, b, T, st, en);
         r.tok0 = st;
         r.len = en - st;
-        r.nc = (int)(chunk_off[b + 1] - chunk_off[b]);
-        r.card0 = chunk_off[b] * H + (int64_t)h * r.nc;
+        int64_t c0 = chunk_off[b], c1 = chunk_off[b + 1];
+        if constexpr (CLAMP) {
+            const int64_t maxc = (T + kChunk - 1) / kChunk + nseq;
+            c0 = c0 < 0 ? 0 : (c0 > maxc ? maxc : c0);
+            c1 = c1 < c0 ? c0 : (c1 > maxc ? maxc : c1);
+            const int64_t need = (r.len + kChunk - 1) / kChunk;
+            if (c1 - c0 > need) c1 = c0 + need;
+        }
+        r.nc = (int)(c1 - c0);
+        r.chunk0 = c0;
+        r.card0 = c0 * H + (int64_t)h * r.nc;
     } else {
         r.tok0 = b * (rs > 0 ? rs : T);
         r.len = T;
         r.nc = NC;
+        r.chunk0 = 0;
         r.card0 = (b * H + h) * (int64_t)NC;
     }
     return r;

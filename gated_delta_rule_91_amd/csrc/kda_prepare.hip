@@ -129,7 +129,8 @@ __global__ __launch_bounds__(kThreads, sizeof(E) == 2 ? 2 : 1) void kda_prepare_
         c = (int)(rest % a.NC);
         b = rest / a.NC;
     }
-    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.row_stride, a.NC, b, h, H);
+    // the plan kernel wrote the chunk offsets just before, in the same call
+    const SeqSpan sp = seq_span<false>(a.cu_seqlens, a.chunk_off, a.T, a.row_stride, a.NC, a.B, b, h, H);
     const int64_t tok0 = (int64_t)c * C;
     char* card = a.ws + (size_t)(sp.card0 + c) * CL::BYTES;
 

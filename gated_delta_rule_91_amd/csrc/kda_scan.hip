@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_scan_kernel(ScanArgs a) {
     if (bh >= BH) return;
     const int64_t b = bh / H;
     const int h = (int)(bh % H);
-    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.row_stride, a.NC, b, h, H);
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.row_stride, a.NC, a.B, b, h, H);
     const int NC = sp.nc;
     const int64_t Tl = sp.len;   // this sequence's tokens
     const bool vcols = tile0 < NT;                        // value columns (else transition columns)

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void kda_summary_wave_kernel(ScanArgs
     if (bh >= BH) return;
     const int64_t b = bh / H;
     const int h = (int)(bh % H);
-    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.row_stride, a.NC, b, h, H);
+    const SeqSpan sp = seq_span(a.cu_seqlens, a.chunk_off, a.T, a.row_stride, a.NC, a.B, b, h, H);
     const int NC = sp.nc;
     const char* cards = a.ws + (size_t)sp.card0 * CL::BYTES;
     lds_c* const ring_l = (lds_c*)ring;

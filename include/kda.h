@@ -181,8 +181,9 @@ kda_status kda_varlen_prepare(const kda_problem* p, int64_t n_seq, const int32_t
 
 /* kda_chunk_scan for a packed batch, with the workspace kda_varlen_prepare
  * filled for the same p, n_seq and cu_seqlens (the chunk offsets it wrote are
- * read back: another workspace or other offsets can send accesses outside the
- * arrays).  g, out: [1, seqlen, H, dv];
+ * read back, clamped to the workspace and to each sequence's length: another
+ * workspace or other offsets give wrong values, never an access outside the
+ * arrays or the workspace).  g, out: [1, seqlen, H, dv];
  * state_in, state_out: [n_seq, H, dk, dv] fp32 or NULL (state_out may equal
  * state_in); an empty sequence passes its state_in through. */
 kda_status kda_varlen_scan(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
@@ -282,9 +283,9 @@ kda_status kda_varlen_backward(const kda_problem* p, int64_t n_seq, const int32_
  * gives kda_varlen_backward's gradients bit for bit (inputs that differ from
  * the first call's give gradients of the wrong point; this is not checked).
  * The second call reads back the chunk offsets the first one wrote into the
- * workspace: a workspace that call did not fill, or other cu_seqlens, can
- * send accesses outside the arrays, so both must be exactly the first
- * call's (as for kda_varlen_scan after kda_varlen_prepare). */
+ * workspace, clamped to the workspace and to each sequence's length: a
+ * workspace that call did not fill, or other cu_seqlens, give wrong values
+ * but no access outside the arrays or the workspace. */
 kda_status kda_varlen_prefill_for_backward(const kda_problem* p, int64_t n_seq, const int32_t* cu_seqlens,
                                            const void* q, const void* k, const void* v, const float* log_alpha,
                                            const float* beta, const void* g, const float* state_in, void* out,
