@@ -330,3 +330,40 @@ def test_varlen_backward_overlapping_offsets_stay_inside_the_workspace():
     assert torch.equal(gr["dstate0"][0:1], full["dstate0"]) and torch.equal(gr["dstate0"][2:3], full["dstate0"])
     assert torch.equal(gr["dstate0"][4:5], one["dstate0"])   # the clamped copy: its first chunk only
     assert torch.equal(gr["dstate0"][1], dst[1]) and torch.equal(gr["dstate0"][3], dst[3])   # empty sequences
+
+
+def test_second_calls_with_other_offsets_stay_inside_the_workspace():
+    """kda_varlen_scan and kda_varlen_backward_after_prefill read back the chunk
+    offsets the first call wrote, clamped to the workspace and to each
+    sequence's length: called with other cu_seqlens than the first call's
+    (sequences longer and shorter than the offsets say), they give wrong
+    values (finite in the per-sequence states and state gradients, which
+    every call writes; token rows the clamped chunks do not cover are not
+    written), with every access inside the arrays and the workspace, and the
+    right cu_seqlens still give the right result after."""
+    H, d, T = 2, 128, 300
+    note("[varlen] second calls with other offsets than the first")
+    inp = make_inputs(1, T, H, d, d, io_dtype="bf16", seed=49, alpha_min=0.9, logit_mu=-1.0)
+    dev = kda.to_device(inp)
+    args = tuple(dev[n] for n in ("q", "k", "v", "log_alpha", "beta", "g"))
+    cu_a = torch.tensor([0, 100, 300], dtype=torch.int32, device="cuda")
+    cu_b = torch.tensor([0, 250, 300], dtype=torch.int32, device="cuda")
+    ws = kda.varlen_prepare(*args[:5], inp.log_alpha_min, cu_a)
+    out, st = kda.varlen_scan(ws, dev["g"], inp.log_alpha_min, cu_b)
+    torch.cuda.synchronize()
+    assert torch.isfinite(st).all()
+    ref_out, ref_st = kda.varlen_prefill(*args, inp.log_alpha_min, cu_a)
+    out2, st2 = kda.varlen_scan(ws, dev["g"], inp.log_alpha_min, cu_a)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref_out) and torch.equal(st2, ref_st)
+    o, s, wsb = kda.varlen_prefill_for_backward(*args, inp.log_alpha_min, cu_a)
+    dout = torch.ones_like(dev["g"])
+    gr = kda.varlen_backward_after_prefill(*args, o, wsb, inp.log_alpha_min, cu_b, d_out=dout,
+                                           d_state=torch.ones_like(s))
+    torch.cuda.synchronize()
+    assert torch.isfinite(gr["dstate0"]).all()
+    ref = kda.varlen_backward(*args, inp.log_alpha_min, cu_a, d_out=dout)
+    got = kda.varlen_backward_after_prefill(*args, o, wsb, inp.log_alpha_min, cu_a, d_out=dout)
+    torch.cuda.synchronize()
+    for n in ref:
+        assert torch.equal(got[n], ref[n]), n
